@@ -1,0 +1,268 @@
+/*
+ * Oracle for the DFlash 2 candidate-selector lattice: plain, slow, fp64, single-threaded C.
+ *
+ * TEST INFRASTRUCTURE. This file is the correctness reference that the GPU library is checked
+ * against. Only the test suite, the smoke check and the benchmark's CPU-baseline leg may load
+ * it. The product library never links, calls or includes anything from here, and nothing here
+ * includes or calls the product library: the two share no code.
+ *
+ * What is computed, and where the pages define it:
+ *   - "DFlash 2: Keep Drafting Parallel" (inco.ai blog), section "A Lightweight Path Selector":
+ *     keep the top 16 candidates per draft position; score every adjacent pair with
+ *     S_t(a,b) = U_t(b) + <A(a) (.) H(h_t), B(b)>, a unary term plus a low-rank bilinear match of a
+ *     predecessor embedding A and a successor embedding B under a context gate H(h_t); then walk
+ *     greedily from the last verified token, following the best successor at each step.
+ *   - "DFlash2 Lands in llama.cpp: What PR #27342 Actually Changes" (ramgpt.org), section
+ *     "What llama.cpp Actually Builds for the Selector": a per-position top-k of the logits, a
+ *     gather of the unary scores of those candidates, a projection of the current hidden state
+ *     through the selector-hidden weight, predecessor rows for the previous position's candidates
+ *     and successor rows for the current candidates; the runtime walk starts with the anchor as
+ *     predecessor and at each position picks the best successor given the chosen predecessor.
+ *
+ * Readings taken where the pages leave a step open (each listed in the design notes):
+ *   - unary = logit - logsumexp over the full vocabulary (log-softmax of the drafter's logits);
+ *   - the gate is linear with no bias, activation or scale: g = h . W_sel, W_sel stored [H, r];
+ *   - A = pred_cb and B = succ_cb, both materialised [V, r] tables;
+ *   - candidate order: higher logit first, equal logits by lower token id (+0 and -0 are equal);
+ *   - the anchor is the single predecessor of position 0, so all k rows of that position's
+ *     lattice are the same row;
+ *   - walk ties go to the lowest candidate index.
+ *
+ * Precision: every input value (fp32 or bf16) converts to double exactly; all arithmetic is in
+ * double. The only library calls are exp and log from libm.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* dtype codes used by the stored inputs: 0 = IEEE binary32, 1 = bfloat16 (upper half of a
+ * binary32, stored as uint16). */
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+
+/* Return codes. */
+enum { ORACLE_OK = 0, ORACLE_BAD_ARG = -1 };
+
+/* Read element i of a stored tensor as a double. bf16 -> binary32 is a 16-bit left shift of the
+ * stored bits; binary32 -> double is exact. */
+static double oracle_value(const void *base, int dtype, size_t i)
+{
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)base)[i];
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static int dtype_ok(int dtype) { return dtype == ORACLE_F32 || dtype == ORACLE_BF16; }
+
+/* Candidate order: token u (logit xu) comes before token v (logit xv) when its logit is higher,
+ * or the logits are equal and its id is lower. Double comparison already treats +0 and -0 as
+ * equal. */
+static int comes_before(double xu, int32_t u, double xv, int32_t v)
+{
+    return xu > xv || (xu == xv && u < v);
+}
+
+/*
+ * Per-row top-k and logsumexp.
+ * logits: [R, V] row-major (dtype), cand_ids: [R, k], unary: [R, k], lse: [R] (may be NULL).
+ * Row i: m = max_v x_v; lse = m + log(sum_v exp(x_v - m)) with a compensated (Neumaier) sum;
+ * cand_ids = the first k tokens of the candidate order, found in one pass that keeps a sorted
+ * array of the best k seen so far; unary_j = x_{cand_j} - lse.
+ */
+int dflash2_ref_topk_lse(const void *logits, int dtype, int R, int V, int k,
+                         int32_t *cand_ids, double *unary, double *lse)
+{
+    if (!logits || !cand_ids || !unary || !dtype_ok(dtype) || R < 0 || V < 1 || k < 1 || k > V)
+        return ORACLE_BAD_ARG;
+    double *best_x = (double *)malloc((size_t)k * sizeof(double));
+    int32_t *best_id = (int32_t *)malloc((size_t)k * sizeof(int32_t));
+    if (!best_x || !best_id) {
+        free(best_x);
+        free(best_id);
+        return ORACLE_BAD_ARG;
+    }
+    for (int row = 0; row < R; ++row) {
+        const size_t base = (size_t)row * (size_t)V;
+
+        double m = -INFINITY;
+        for (int v = 0; v < V; ++v) {
+            double x = oracle_value(logits, dtype, base + v);
+            if (x > m)
+                m = x;
+        }
+
+        double sum = 0.0, comp = 0.0;
+        for (int v = 0; v < V; ++v) {
+            double t = exp(oracle_value(logits, dtype, base + v) - m);
+            double y = sum + t;
+            if (fabs(sum) >= fabs(t))
+                comp += (sum - y) + t;
+            else
+                comp += (t - y) + sum;
+            sum = y;
+        }
+        const double row_lse = m + log(sum + comp);
+
+        int n = 0;
+        for (int v = 0; v < V; ++v) {
+            double x = oracle_value(logits, dtype, base + v);
+            if (n == k && !comes_before(x, v, best_x[k - 1], best_id[k - 1]))
+                continue;
+            int pos = (n < k) ? n : k - 1; /* when full, the current last entry is dropped */
+            while (pos > 0 && comes_before(x, v, best_x[pos - 1], best_id[pos - 1])) {
+                best_x[pos] = best_x[pos - 1];
+                best_id[pos] = best_id[pos - 1];
+                --pos;
+            }
+            best_x[pos] = x;
+            best_id[pos] = v;
+            if (n < k)
+                ++n;
+        }
+
+        for (int j = 0; j < k; ++j) {
+            cand_ids[(size_t)row * k + j] = best_id[j];
+            unary[(size_t)row * k + j] = best_x[j] - row_lse;
+        }
+        if (lse)
+            lse[row] = row_lse;
+    }
+    free(best_x);
+    free(best_id);
+    return ORACLE_OK;
+}
+
+/*
+ * Context gate: g[i][d] = sum_h hidden[i][h] * W_sel[h][d].
+ * hidden: [R, H], W_sel: [H, r] (both act_dtype), g: [R, r].
+ */
+int dflash2_ref_gate(const void *hidden, const void *W_sel, int act_dtype, int R, int H, int r,
+                     double *g)
+{
+    if (!hidden || !W_sel || !g || !dtype_ok(act_dtype) || R < 0 || H < 1 || r < 1)
+        return ORACLE_BAD_ARG;
+    for (int i = 0; i < R; ++i)
+        for (int d = 0; d < r; ++d) {
+            double acc = 0.0;
+            for (int h = 0; h < H; ++h)
+                acc += oracle_value(hidden, act_dtype, (size_t)i * H + h) *
+                       oracle_value(W_sel, act_dtype, (size_t)h * r + d);
+            g[(size_t)i * r + d] = acc;
+        }
+    return ORACLE_OK;
+}
+
+/*
+ * Transition lattice.
+ * edges[b][p][i][j] = unary[b][p][j] + sum_d pred_cb[prev_i][d] * succ_cb[cand_j][d] * g[b][p][d]
+ * with cand_j = cand_ids[b][p][j], prev_i = anchor_ids[b] when p = 0 (every i) and
+ * prev_i = cand_ids[b][p-1][i] otherwise.
+ * cand_ids, unary: [B, L, k]; g: [B, L, r]; pred_cb, succ_cb: [V, r] (cb_dtype); anchor_ids: [B];
+ * edges: [B, L, k, k].
+ */
+int dflash2_ref_lattice(const int32_t *cand_ids, const double *unary, const double *g,
+                        const void *pred_cb, const void *succ_cb, int cb_dtype,
+                        const int32_t *anchor_ids, int B, int L, int V, int r, int k,
+                        double *edges)
+{
+    if (!cand_ids || !unary || !g || !pred_cb || !succ_cb || !anchor_ids || !edges ||
+        !dtype_ok(cb_dtype) || B < 0 || L < 1 || V < 1 || r < 1 || k < 1)
+        return ORACLE_BAD_ARG;
+    for (int b = 0; b < B; ++b) {
+        if (anchor_ids[b] < 0 || anchor_ids[b] >= V)
+            return ORACLE_BAD_ARG;
+        for (int p = 0; p < L; ++p) {
+            const size_t row = (size_t)b * L + p;
+            for (int i = 0; i < k; ++i) {
+                const int32_t prev = (p == 0) ? anchor_ids[b] : cand_ids[(row - 1) * k + i];
+                if (prev < 0 || prev >= V)
+                    return ORACLE_BAD_ARG;
+                for (int j = 0; j < k; ++j) {
+                    const int32_t cand = cand_ids[row * k + j];
+                    if (cand < 0 || cand >= V)
+                        return ORACLE_BAD_ARG;
+                    double acc = 0.0;
+                    for (int d = 0; d < r; ++d)
+                        acc += oracle_value(pred_cb, cb_dtype, (size_t)prev * r + d) *
+                               oracle_value(succ_cb, cb_dtype, (size_t)cand * r + d) *
+                               g[row * r + d];
+                    edges[(row * k + i) * k + j] = unary[row * k + j] + acc;
+                }
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Greedy walk. For each sequence: the predecessor index starts at 0 (at position 0 every lattice
+ * row is the anchor's row); at position p the chosen index is the lowest j with the largest
+ * edges[b][p][prev][j]; path = cand_ids[b][p][j]; then prev = j.
+ * Diagnostics: path_idx [B, L] (chosen j), margin [B, L] (best edge minus the best other edge
+ * in the same row, +inf when k = 1), score [B] (sum of the chosen edges). Any diagnostic
+ * pointer may be NULL.
+ */
+int dflash2_ref_walk(const double *edges, const int32_t *cand_ids, int B, int L, int k,
+                     int32_t *path, int32_t *path_idx, double *margin, double *score)
+{
+    if (!edges || !cand_ids || !path || B < 0 || L < 1 || k < 1)
+        return ORACLE_BAD_ARG;
+    for (int b = 0; b < B; ++b) {
+        int prev = 0;
+        double total = 0.0;
+        for (int p = 0; p < L; ++p) {
+            const size_t row = (size_t)b * L + p;
+            const double *e = edges + (row * k + prev) * k;
+            int best = 0;
+            for (int j = 1; j < k; ++j)
+                if (e[j] > e[best])
+                    best = j;
+            double second = -INFINITY;
+            for (int j = 0; j < k; ++j)
+                if (j != best && e[j] > second)
+                    second = e[j];
+            path[row] = cand_ids[row * k + best];
+            if (path_idx)
+                path_idx[row] = best;
+            if (margin)
+                margin[row] = (k == 1) ? INFINITY : e[best] - second;
+            total += e[best];
+            prev = best;
+        }
+        if (score)
+            score[b] = total;
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * The whole selector: top-k + logsumexp, gate, lattice, walk, in that order, on host buffers.
+ * Outputs: cand_ids [B,L,k], unary [B,L,k], edges [B,L,k,k], path [B,L]; optional diagnostics
+ * lse [B,L], path_idx [B,L], margin [B,L], score [B] (NULL to skip).
+ */
+int dflash2_ref_select(const void *logits, int logits_dtype, const void *hidden, int act_dtype,
+                       const void *W_sel, const void *pred_cb, const void *succ_cb, int cb_dtype,
+                       const int32_t *anchor_ids, int B, int L, int V, int H, int r, int k,
+                       int32_t *cand_ids, double *unary, double *edges, int32_t *path,
+                       double *lse, int32_t *path_idx, double *margin, double *score)
+{
+    if (B < 0 || L < 1)
+        return ORACLE_BAD_ARG;
+    const int R = B * L;
+    double *g = (double *)malloc(((size_t)R * r + 1) * sizeof(double));
+    if (!g)
+        return ORACLE_BAD_ARG;
+    int rc = dflash2_ref_topk_lse(logits, logits_dtype, R, V, k, cand_ids, unary, lse);
+    if (rc == ORACLE_OK)
+        rc = dflash2_ref_gate(hidden, W_sel, act_dtype, R, H, r, g);
+    if (rc == ORACLE_OK)
+        rc = dflash2_ref_lattice(cand_ids, unary, g, pred_cb, succ_cb, cb_dtype, anchor_ids, B, L,
+                                 V, r, k, edges);
+    if (rc == ORACLE_OK)
+        rc = dflash2_ref_walk(edges, cand_ids, B, L, k, path, path_idx, margin, score);
+    free(g);
+    return rc;
+}
