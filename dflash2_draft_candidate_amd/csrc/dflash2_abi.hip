@@ -1,0 +1,189 @@
+// The C ABI (include/dflash2.h): host-side validation, workspace layout and launches.
+// Nothing here allocates device memory or synchronises; all work goes to the caller's stream.
+#include "dflash2.h"
+
+#include <limits.h>
+
+#include "kernels.h"
+
+namespace {
+
+using namespace dflash2;
+
+constexpr size_t kAlign = 256;  // workspace sub-buffer alignment
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dtype_ok(int dt) { return dt == DFLASH2_F32 || dt == DFLASH2_BF16; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DFLASH2_OK : DFLASH2_ERR_HIP; }
+
+// Sizes shared by select and its stages; 0 = valid.
+int check_rows(int R, int V, int k) {
+    if (R < 1 || V < 1 || k < 1 || k > DFLASH2_MAX_K || k > V) return DFLASH2_ERR_INVALID_ARG;
+    return DFLASH2_OK;
+}
+
+int check_ptrs(std::initializer_list<const void *> ptrs) {
+    for (const void *p : ptrs)
+        if (!p) return DFLASH2_ERR_INVALID_ARG;
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return DFLASH2_ERR_ALIGNMENT;
+    return DFLASH2_OK;
+}
+
+int64_t rows_of(int B, int L) { return (int64_t)B * L; }
+
+struct SelectLayout {
+    size_t lse, g, topk, gate, total;
+};
+
+// Workspace of dflash2_select for one logits dtype: lse [R] | g [R, r] | K1 partials | K2 partials.
+SelectLayout select_layout(int R, int V, int H, int r, int logits_dtype) {
+    SelectLayout s;
+    size_t off = 0;
+    s.lse = off;
+    off += round_up((size_t)R * sizeof(float));
+    s.g = off;
+    off += round_up((size_t)R * r * sizeof(float));
+    s.topk = off;
+    off += round_up(topk_workspace_bytes(plan_topk(R, V, logits_dtype == DFLASH2_F32 ? 4 : 2), R));
+    s.gate = off;
+    off += round_up(gate_workspace_bytes(plan_gate(R, H, r), R, r));
+    s.total = off;
+    return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dflash2_version(void) { return DFLASH2_ABI_VERSION; }
+
+const char *dflash2_status_string(int status) {
+    switch (status) {
+    case DFLASH2_OK: return "ok";
+    case DFLASH2_ERR_INVALID_ARG: return "invalid argument (size, dtype or NULL pointer)";
+    case DFLASH2_ERR_UNSUPPORTED: return "unsupported request";
+    case DFLASH2_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+    case DFLASH2_ERR_WORKSPACE: return "workspace missing or too small";
+    case DFLASH2_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+    }
+}
+
+size_t dflash2_topk_lse_workspace_bytes(int R, int V, int k, int logits_dtype) {
+    if (check_rows(R, V, k) != DFLASH2_OK || !dtype_ok(logits_dtype)) return 0;
+    return topk_workspace_bytes(plan_topk(R, V, logits_dtype == DFLASH2_F32 ? 4 : 2), R);
+}
+
+int dflash2_topk_lse(const void *logits, int logits_dtype, int R, int V, int k, int32_t *cand_ids,
+                     float *unary, float *lse, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    int rc = check_rows(R, V, k);
+    if (rc) return rc;
+    if (!dtype_ok(logits_dtype)) return DFLASH2_ERR_INVALID_ARG;
+    if ((int64_t)R * V / V != R) return DFLASH2_ERR_INVALID_ARG;
+    if ((rc = check_ptrs({logits, cand_ids, unary}))) return rc;
+    if (lse && !aligned16(lse)) return DFLASH2_ERR_ALIGNMENT;
+    const size_t need = dflash2_topk_lse_workspace_bytes(R, V, k, logits_dtype);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return DFLASH2_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return DFLASH2_ERR_ALIGNMENT;
+    }
+    return hip_status(launch_topk_lse(logits, logits_dtype, R, V, k, cand_ids, unary, lse,
+                                      workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t dflash2_gate_workspace_bytes(int R, int H, int r) {
+    if (R < 1 || H < 1 || r < 1 || r > DFLASH2_MAX_R) return 0;
+    return gate_workspace_bytes(plan_gate(R, H, r), R, r);
+}
+
+int dflash2_gate(const void *hidden, const void *W_sel, int act_dtype, int R, int H, int r,
+                 float *g, void *workspace, size_t workspace_bytes, void *stream) {
+    if (R < 1 || H < 1 || r < 1 || r > DFLASH2_MAX_R || !dtype_ok(act_dtype))
+        return DFLASH2_ERR_INVALID_ARG;
+    int rc = check_ptrs({hidden, W_sel, g});
+    if (rc) return rc;
+    const size_t need = act_dtype == DFLASH2_BF16 ? dflash2_gate_workspace_bytes(R, H, r) : 0;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return DFLASH2_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return DFLASH2_ERR_ALIGNMENT;
+    }
+    return hip_status(launch_gate(hidden, W_sel, act_dtype, R, H, r, g, workspace,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+int dflash2_lattice(const int32_t *cand_ids, const float *unary, const float *g,
+                    const void *pred_cb, const void *succ_cb, int cb_dtype,
+                    const int32_t *anchor_ids, int B, int L, int V, int r, int k, float *edges,
+                    void *stream) {
+    if (B < 1 || L < 1 || V < 1 || r < 1 || r > DFLASH2_MAX_R || k < 1 || k > DFLASH2_MAX_K ||
+        !dtype_ok(cb_dtype) || rows_of(B, L) > INT_MAX)
+        return DFLASH2_ERR_INVALID_ARG;
+    int rc = check_ptrs({cand_ids, unary, g, pred_cb, succ_cb, anchor_ids, edges});
+    if (rc) return rc;
+    return hip_status(launch_lattice(cand_ids, unary, g, pred_cb, succ_cb, cb_dtype, anchor_ids, B,
+                                     L, V, r, k, edges, static_cast<hipStream_t>(stream)));
+}
+
+int dflash2_walk(const float *edges, const int32_t *cand_ids, int B, int L, int k, int32_t *path,
+                 int32_t *path_idx, void *stream) {
+    if (B < 1 || L < 1 || k < 1 || k > DFLASH2_MAX_K || rows_of(B, L) > INT_MAX)
+        return DFLASH2_ERR_INVALID_ARG;
+    int rc = check_ptrs({edges, cand_ids, path});
+    if (rc) return rc;
+    if (path_idx && !aligned16(path_idx)) return DFLASH2_ERR_ALIGNMENT;
+    return hip_status(launch_walk(edges, cand_ids, B, L, k, path, path_idx,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+size_t dflash2_workspace_bytes(int B, int L, int V, int H, int r, int k) {
+    if (B < 1 || L < 1 || H < 1 || r < 1 || r > DFLASH2_MAX_R || rows_of(B, L) > INT_MAX ||
+        check_rows((int)rows_of(B, L), V, k) != DFLASH2_OK)
+        return 0;
+    const int R = (int)rows_of(B, L);
+    const size_t a = select_layout(R, V, H, r, DFLASH2_F32).total;
+    const size_t b = select_layout(R, V, H, r, DFLASH2_BF16).total;
+    return a > b ? a : b;
+}
+
+int dflash2_select(const void *logits, int logits_dtype, const void *hidden, int act_dtype,
+                   const void *W_sel, const void *pred_cb, const void *succ_cb, int cb_dtype,
+                   const int32_t *anchor_ids, int B, int L, int V, int H, int r, int k,
+                   int32_t *cand_ids, float *unary, float *edges, int32_t *path, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    if (B < 1 || L < 1 || H < 1 || r < 1 || r > DFLASH2_MAX_R || rows_of(B, L) > INT_MAX)
+        return DFLASH2_ERR_INVALID_ARG;
+    const int R = (int)rows_of(B, L);
+    int rc = check_rows(R, V, k);
+    if (rc) return rc;
+    if (!dtype_ok(logits_dtype) || !dtype_ok(act_dtype) || !dtype_ok(cb_dtype))
+        return DFLASH2_ERR_INVALID_ARG;
+    if ((rc = check_ptrs({logits, hidden, W_sel, pred_cb, succ_cb, anchor_ids, cand_ids, unary,
+                          edges, path})))
+        return rc;
+    const size_t need = dflash2_workspace_bytes(B, L, V, H, r, k);
+    if (!workspace || workspace_bytes < need) return DFLASH2_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return DFLASH2_ERR_ALIGNMENT;
+
+    const SelectLayout lay = select_layout(R, V, H, r, logits_dtype);
+    char *ws = static_cast<char *>(workspace);
+    float *lse = reinterpret_cast<float *>(ws + lay.lse);
+    float *g = reinterpret_cast<float *>(ws + lay.g);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    hipError_t e = launch_topk_lse(logits, logits_dtype, R, V, k, cand_ids, unary, lse,
+                                   ws + lay.topk, s);
+    if (e == hipSuccess) e = launch_gate(hidden, W_sel, act_dtype, R, H, r, g, ws + lay.gate, s);
+    if (e == hipSuccess)
+        e = launch_lattice(cand_ids, unary, g, pred_cb, succ_cb, cb_dtype, anchor_ids, B, L, V, r,
+                           k, edges, s);
+    if (e == hipSuccess) e = launch_walk(edges, cand_ids, B, L, k, path, nullptr, s);
+    return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// Internal launch interface between the C ABI (dflash2_abi.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dflash2 {
+
+// ---- K1: top-k + logsumexp -----------------------------------------------------------------
+struct TopkPlan {
+    int waves;   // waves per workgroup
+    int slices;  // workgroups per row; > 1 adds a merge kernel and needs workspace
+};
+TopkPlan plan_topk(int R, int V, int elem_bytes);
+size_t topk_workspace_bytes(const TopkPlan &plan, int R);
+hipError_t launch_topk_lse(const void *logits, int logits_dtype, int R, int V, int k,
+                           int32_t *cand_ids, float *unary, float *lse, void *workspace,
+                           hipStream_t stream);
+
+// ---- K2: gate GEMM ---------------------------------------------------------------------------
+struct GatePlan {
+    int ksplit;  // workgroups along H; > 1 adds a reduction kernel and needs workspace
+};
+GatePlan plan_gate(int R, int H, int r);
+size_t gate_workspace_bytes(const GatePlan &plan, int R, int r);
+hipError_t launch_gate(const void *hidden, const void *W_sel, int act_dtype, int R, int H, int r,
+                       float *g, void *workspace, hipStream_t stream);
+
+// ---- K3: lattice -----------------------------------------------------------------------------
+hipError_t launch_lattice(const int32_t *cand_ids, const float *unary, const float *g,
+                          const void *pred_cb, const void *succ_cb, int cb_dtype,
+                          const int32_t *anchor_ids, int B, int L, int V, int r, int k,
+                          float *edges, hipStream_t stream);
+
+// ---- K4: walk --------------------------------------------------------------------------------
+hipError_t launch_walk(const float *edges, const int32_t *cand_ids, int B, int L, int k,
+                       int32_t *path, int32_t *path_idx, hipStream_t stream);
+
+}  // namespace dflash2

@@ -1,0 +1,155 @@
+/*
+ * dflash2.h - C ABI of the MI355X (gfx950) DFlash 2 candidate-selector library (libdflash2.so).
+ *
+ * What it computes. For every position of a speculative draft block the selector keeps the
+ * drafter's top-k candidate tokens, scores every adjacent candidate pair and walks the resulting
+ * lattice greedily:
+ *   - "DFlash 2: Keep Drafting Parallel" (inco.ai blog), section "A Lightweight Path Selector":
+ *     top 16 candidates per position; pair score S_t(a,b) = U_t(b) + <A(a) (.) H(h_t), B(b)>, a
+ *     unary term plus a low-rank bilinear match of a predecessor embedding A(a) and a successor
+ *     embedding B(b) under a context gate H(h_t); a greedy walk from the last verified token.
+ *   - "DFlash2 Lands in llama.cpp: What PR #27342 Actually Changes" (ramgpt.org), section "What
+ *     llama.cpp Actually Builds for the Selector": per-position top-k of the logits, the unary
+ *     scores of the candidates, the hidden state projected through the selector-hidden weight,
+ *     predecessor codebook rows for the previous position's candidates and successor rows for
+ *     the current ones; the walk starts from the anchor and follows the best successor.
+ * Readings fixed by this library where the pages leave a step open:
+ *   unary = logit - logsumexp(all V logits of the row); g = h . W_sel (linear, no bias/scale);
+ *   A = pred_cb, B = succ_cb; candidate order = higher logit first, equal logits by lower id,
+ *   +0 == -0; the anchor is the single predecessor of position 0; walk ties go to the lowest
+ *   candidate index.
+ *
+ * Conventions for every entry point.
+ *   - Tensors are dense, row-major and contiguous. "Device" pointers are GPU memory the caller
+ *     owns (e.g. from PyTorch); the library never allocates, frees or keeps them.
+ *   - Every pointer argument must be 16-byte aligned (DFLASH2_ERR_ALIGNMENT otherwise).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call returns
+ *     without synchronising. Outputs are valid once the stream reaches that point.
+ *   - Arguments are validated on the host before anything is launched; on any error nothing is
+ *     enqueued and outputs are untouched. A failed launch returns DFLASH2_ERR_HIP.
+ *   - Device-side preconditions (not checked on the host): logits are finite with |x| < 1e37;
+ *     ids in anchor_ids / cand_ids lie in [0, V). A lattice row whose predecessor or candidate
+ *     id lies outside [0, V) is written as NaN instead of being read out of bounds.
+ *   - Concurrent calls on different streams are safe when each has its own workspace.
+ *   - Results are deterministic: the same inputs give bit-identical outputs on every run.
+ */
+#ifndef DFLASH2_H
+#define DFLASH2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DFLASH2_ABI_VERSION 1
+#define DFLASH2_MAX_K 64  /* largest top-k */
+#define DFLASH2_MAX_R 256 /* largest codebook rank r */
+
+typedef enum dflash2_dtype {
+    DFLASH2_F32 = 0,  /* IEEE binary32 */
+    DFLASH2_BF16 = 1  /* bfloat16: the upper 16 bits of a binary32 */
+} dflash2_dtype;
+
+typedef enum dflash2_status {
+    DFLASH2_OK = 0,
+    DFLASH2_ERR_INVALID_ARG = -1, /* a size or dtype out of range, or a NULL pointer */
+    DFLASH2_ERR_UNSUPPORTED = -2, /* a valid request this build does not implement */
+    DFLASH2_ERR_ALIGNMENT = -3,   /* a pointer is not 16-byte aligned */
+    DFLASH2_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
+    DFLASH2_ERR_HIP = -5          /* the HIP runtime reported an error at launch */
+} dflash2_status;
+
+/* ABI version of the loaded library (DFLASH2_ABI_VERSION). */
+int dflash2_version(void);
+
+/* Static description of a status code (never NULL). */
+const char *dflash2_status_string(int status);
+
+/*
+ * dflash2_select - the whole selector in one call: top-k + logsumexp, gate, lattice, walk.
+ *
+ *   logits      [B, L, V]  logits_dtype, device. Row (b, p) is the drafter's output at draft
+ *                          position p of sequence b (the row of hidden[b][p]).
+ *   hidden      [B, L, H]  act_dtype, device. The drafter's final hidden state per position.
+ *   W_sel       [H, r]     act_dtype, device. Selector-hidden projection; g = hidden . W_sel.
+ *   pred_cb     [V, r]     cb_dtype, device. Predecessor codebook A.
+ *   succ_cb     [V, r]     cb_dtype, device. Successor codebook B.
+ *   anchor_ids  [B]        int32, device. Last verified token of each sequence.
+ *   B, L, V, H, r, k       B, L, V, H >= 1; 1 <= r <= DFLASH2_MAX_R; 1 <= k <= min(V, DFLASH2_MAX_K).
+ * Outputs (device, written in full):
+ *   cand_ids    [B, L, k]     int32. The first k tokens of the candidate order.
+ *   unary       [B, L, k]     float. logit - logsumexp(row), in candidate order.
+ *   edges       [B, L, k, k]  float. edges[b][p][i][j] = unary[b][p][j]
+ *                               + sum_d pred_cb[prev_i][d] * succ_cb[cand_j][d] * g[b][p][d],
+ *                             prev_i = cand_ids[b][p-1][i] for p >= 1; for p = 0 every row i
+ *                             uses prev = anchor_ids[b], so the k rows are identical.
+ *   path        [B, L]        int32 token ids of the greedy walk: j_0 = argmax_j edges[b][0][0][j],
+ *                             j_p = argmax_j edges[b][p][j_{p-1}][j] (lowest j on ties),
+ *                             path[b][p] = cand_ids[b][p][j_p].
+ *   workspace / workspace_bytes: device scratch of at least dflash2_workspace_bytes(...) bytes
+ *                             (may be NULL when that is 0); contents need no initialisation and
+ *                             are overwritten.
+ * Scores accumulate in fp32.
+ */
+size_t dflash2_workspace_bytes(int B, int L, int V, int H, int r, int k);
+
+int dflash2_select(const void *logits, int logits_dtype, const void *hidden, int act_dtype,
+                   const void *W_sel, const void *pred_cb, const void *succ_cb, int cb_dtype,
+                   const int32_t *anchor_ids, int B, int L, int V, int H, int r, int k,
+                   int32_t *cand_ids, float *unary, float *edges, int32_t *path, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/*
+ * The four stages, callable one by one (same conventions; dflash2_select runs exactly these).
+ *
+ * dflash2_topk_lse - per row of logits [R, V]: cand_ids [R, k] and unary [R, k] as above, and
+ *   (if lse is not NULL) lse [R] = logsumexp of the row. Needs
+ *   dflash2_topk_lse_workspace_bytes(R, V, k, logits_dtype) bytes of workspace.
+ *   Sources: blog "A Lightweight Path Selector" (top 16 per position, unary term); ramgpt
+ *   "What llama.cpp Actually Builds for the Selector" (per-position top-k, gathered unary).
+ */
+size_t dflash2_topk_lse_workspace_bytes(int R, int V, int k, int logits_dtype);
+
+int dflash2_topk_lse(const void *logits, int logits_dtype, int R, int V, int k, int32_t *cand_ids,
+                     float *unary, float *lse, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/*
+ * dflash2_gate - g [R, r] (float) = hidden [R, H] . W_sel [H, r], act_dtype inputs, fp32
+ *   accumulation (bf16 inputs run on the matrix cores). Needs dflash2_gate_workspace_bytes(R, H, r)
+ *   bytes of workspace. Source: blog "A Lightweight Path Selector" (context gate H(h_t)); ramgpt
+ *   "What llama.cpp Actually Builds for the Selector" (hidden state projected through the
+ *   selector-hidden weight).
+ */
+size_t dflash2_gate_workspace_bytes(int R, int H, int r);
+
+int dflash2_gate(const void *hidden, const void *W_sel, int act_dtype, int R, int H, int r,
+                 float *g, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * dflash2_lattice - edges [B, L, k, k] (float) from cand_ids [B, L, k] (int32), unary [B, L, k]
+ *   (float), g [B, L, r] (float), pred_cb / succ_cb [V, r] (cb_dtype) and anchor_ids [B], as in
+ *   dflash2_select. No workspace. Source: blog "A Lightweight Path Selector" (eq. S_t(a,b));
+ *   ramgpt "What llama.cpp Actually Builds for the Selector" (codebook gathers, anchor).
+ */
+int dflash2_lattice(const int32_t *cand_ids, const float *unary, const float *g,
+                    const void *pred_cb, const void *succ_cb, int cb_dtype,
+                    const int32_t *anchor_ids, int B, int L, int V, int r, int k, float *edges,
+                    void *stream);
+
+/*
+ * dflash2_walk - path [B, L] (int32 token ids) from edges [B, L, k, k] and cand_ids [B, L, k], as
+ *   in dflash2_select; path_idx [B, L] (int32, may be NULL) receives the chosen candidate index
+ *   j_p. No workspace. Source: blog "A Lightweight Path Selector" (greedy walk from the last
+ *   verified token); ramgpt "What llama.cpp Actually Builds for the Selector" (runtime walk).
+ */
+int dflash2_walk(const float *edges, const int32_t *cand_ids, int B, int L, int k, int32_t *path,
+                 int32_t *path_idx, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH2_H */

@@ -1,0 +1,271 @@
+"""HIP path vs the oracle (needs an MI355X). Every call goes through the C ABI via the binding.
+
+Inputs are seeded and synthetic. Stage tests feed the same stored inputs to both sides; the
+end-to-end tests run each workload at its full size and compare every output under the rules in
+parity.py.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import assert_close, assert_ids_equal, check_path, check_select
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import dflash2_draft_candidate_amd as d2
+    return d2
+
+
+@pytest.fixture(scope="module")
+def ref():
+    return oracle.default()
+
+
+def to_dev(a):
+    return synth.as_torch(a, DEV)
+
+
+def to_np(t):
+    return synth.from_torch(t)
+
+
+def store(x, dtype):
+    return synth.to_bf16(x) if dtype == "bf16" else np.ascontiguousarray(x, np.float32)
+
+
+# ------------------------------------------------------------------------------ K1: top-k + lse
+
+def _logits(case, R, V, dtype, seed):
+    rng = np.random.default_rng(seed)
+    if case == "normal":
+        x = rng.normal(0, 3, (R, V))
+    elif case == "ties":
+        x = rng.integers(-4, 5, (R, V)).astype(np.float64)
+    elif case == "signed_zero":
+        x = -np.abs(rng.normal(1, 1, (R, V)))
+        zeros = rng.random((R, V)) < 0.05
+        x[zeros] = np.where(rng.random(zeros.sum()) < 0.5, -0.0, 0.0)
+    elif case == "constant":
+        x = np.full((R, V), 1.5)
+    elif case == "ascending":
+        x = np.tile(np.linspace(-8, 8, V), (R, 1))
+    elif case == "descending":
+        x = np.tile(np.linspace(8, -8, V), (R, 1))
+    elif case == "peaked":
+        x = rng.normal(0, 0.1, (R, V))
+        x[np.arange(R), rng.integers(0, V, R)] += 12.0
+    else:
+        raise ValueError(case)
+    return store(x.astype(np.float32), dtype)
+
+
+TOPK_CASES = [
+    # (case, R, V, k, dtype)
+    ("normal", 4, 1024, 4, "f32"),
+    ("normal", 7, 1021, 16, "bf16"),
+    ("normal", 7, 1021, 16, "f32"),
+    ("normal", 5, 37, 37, "f32"),
+    ("normal", 9, 5, 3, "bf16"),
+    ("normal", 3, 1, 1, "f32"),
+    ("normal", 8, 5000, 1, "bf16"),
+    ("normal", 6, 70001, 64, "f32"),
+    ("normal", 16, 151936, 16, "bf16"),
+    ("normal", 3, 262144, 32, "bf16"),
+    ("ties", 8, 3000, 20, "bf16"),
+    ("ties", 5, 40000, 64, "f32"),
+    ("signed_zero", 6, 2000, 24, "f32"),
+    ("signed_zero", 6, 2000, 24, "bf16"),
+    ("constant", 3, 4096, 8, "f32"),
+    ("ascending", 2, 20000, 16, "f32"),
+    ("descending", 2, 20000, 16, "bf16"),
+    ("peaked", 64, 151936, 32, "f32"),
+]
+
+
+@pytest.mark.parametrize("case,R,V,k,dtype", TOPK_CASES,
+                         ids=[f"{c}-R{R}-V{V}-k{k}-{d}" for c, R, V, k, d in TOPK_CASES])
+def test_topk_lse(lib, ref, case, R, V, k, dtype):
+    log(f"topk_lse {case} R={R} V={V} k={k} {dtype}")
+    x = _logits(case, R, V, dtype, seed=R * 1000 + V)
+    ids, unary, lse = lib.topk_lse(to_dev(x), k)
+    torch.cuda.synchronize()
+    rid, runary, rlse = ref.topk_lse(x, k)
+    assert_ids_equal(to_np(ids), rid, "cand_ids")
+    assert_close(to_np(unary), runary, "unary")
+    assert_close(to_np(lse), rlse, "lse", rtol=1e-6, atol=1e-5)
+
+
+# --------------------------------------------------------------------------------- K2: gate
+
+GATE_CASES = [(4, 64, 16, "f32"), (16, 4096, 64, "bf16"), (1024, 4096, 64, "bf16"),
+              (33, 100, 24, "bf16"), (5, 5376, 128, "bf16"), (17, 256, 256, "bf16"),
+              (3, 40, 1, "bf16"), (2048, 4096, 64, "bf16"), (7, 300, 33, "f32")]
+
+
+@pytest.mark.parametrize("R,H,r,dtype", GATE_CASES, ids=[f"R{a}-H{b}-r{c}-{d}" for a, b, c, d in GATE_CASES])
+def test_gate(lib, ref, R, H, r, dtype):
+    log(f"gate R={R} H={H} r={r} {dtype}")
+    rng = np.random.default_rng(R + H + r)
+    h = store(rng.normal(0, 1, (R, H)).astype(np.float32), dtype)
+    w = store((rng.normal(0, 1, (H, r)) / math.sqrt(H)).astype(np.float32), dtype)
+    g = lib.gate(to_dev(h), to_dev(w))
+    torch.cuda.synchronize()
+    want = ref.gate(h, w)
+    hw = synth.bf16_to_f32(h) if dtype == "bf16" else h
+    ww = synth.bf16_to_f32(w) if dtype == "bf16" else w
+    scale = np.abs(hw.astype(np.float64)) @ np.abs(ww.astype(np.float64))
+    # fp32 accumulation of H products: bounded well inside 1e-5 of the absolute sum
+    err = np.abs(to_np(g).astype(np.float64) - want)
+    assert np.all(err <= 1e-5 * scale + 1e-30), f"gate error {np.max(err / (scale + 1e-30)):.3e} of |h||w|"
+
+
+# ------------------------------------------------------------------------------ K3: lattice
+
+def _lattice_inputs(B, L, V, r, k, cb_dtype, seed):
+    rng = np.random.default_rng(seed)
+    cand = np.stack([np.stack([rng.choice(V, k, replace=False) for _ in range(L)])
+                     for _ in range(B)]).astype(np.int32)
+    unary = rng.normal(-8, 3, (B, L, k)).astype(np.float32)
+    g = rng.normal(0, 1, (B, L, r)).astype(np.float32)
+    pred = store((rng.normal(0, 1, (V, r)) / math.sqrt(r)).astype(np.float32), cb_dtype)
+    succ = store((rng.normal(0, 1, (V, r)) / math.sqrt(r)).astype(np.float32), cb_dtype)
+    anchor = rng.integers(0, V, B).astype(np.int32)
+    return cand, unary, g, pred, succ, anchor
+
+
+LATTICE_CASES = [(1, 4, 1024, 16, 4, "f32"), (4, 16, 151936, 64, 16, "bf16"),
+                 (3, 5, 500, 24, 7, "bf16"), (2, 3, 5000, 256, 64, "bf16"),
+                 (2, 2, 100, 1, 3, "f32"), (8, 8, 151936, 64, 32, "bf16"), (1, 1, 10, 5, 1, "f32")]
+
+
+@pytest.mark.parametrize("B,L,V,r,k,cb", LATTICE_CASES,
+                         ids=[f"B{a}-L{b}-V{c}-r{d}-k{e}-{f}" for a, b, c, d, e, f in LATTICE_CASES])
+def test_lattice(lib, ref, B, L, V, r, k, cb):
+    log(f"lattice B={B} L={L} V={V} r={r} k={k} {cb}")
+    cand, unary, g, pred, succ, anchor = _lattice_inputs(B, L, V, r, k, cb, seed=B * L * k + r)
+    edges = lib.lattice(to_dev(cand), to_dev(unary), to_dev(g), to_dev(pred), to_dev(succ),
+                        to_dev(anchor))
+    torch.cuda.synchronize()
+    want = ref.lattice(cand, unary.astype(np.float64), g.astype(np.float64), pred, succ, anchor)
+    assert_close(to_np(edges), want, "edges")
+    e = to_np(edges)
+    for b in range(B):
+        assert np.all(e[b, 0] == e[b, 0, 0][None, :]), "position-0 rows must be identical"
+
+
+def test_lattice_bad_anchor_is_nan(lib):
+    cand, unary, g, pred, succ, anchor = _lattice_inputs(2, 3, 200, 16, 4, "bf16", seed=9)
+    anchor[1] = 200  # out of range: its position-0 row must be NaN, nothing read out of bounds
+    edges = to_np(lib.lattice(to_dev(cand), to_dev(unary), to_dev(g), to_dev(pred), to_dev(succ),
+                              to_dev(anchor)))
+    assert np.all(np.isnan(edges[1, 0])) and np.all(np.isfinite(edges[0])) and \
+        np.all(np.isfinite(edges[1, 1:]))
+
+
+# --------------------------------------------------------------------------------- K4: walk
+
+WALK_CASES = [(2, 4, 4), (3, 16, 16), (5, 8, 32), (2, 5, 64), (4, 40, 16), (3, 7, 1), (1, 1, 3)]
+
+
+@pytest.mark.parametrize("B,L,k", WALK_CASES, ids=[f"B{a}-L{b}-k{c}" for a, b, c in WALK_CASES])
+def test_walk(lib, ref, B, L, k):
+    log(f"walk B={B} L={L} k={k}")
+    rng = np.random.default_rng(B * 100 + L * 10 + k)
+    for edges in (rng.integers(-3, 4, (B, L, k, k)).astype(np.float32),   # exact ties
+                  rng.normal(0, 2, (B, L, k, k)).astype(np.float32)):
+        edges[:, 0] = edges[:, 0, :1]
+        cand = rng.integers(0, 151936, (B, L, k)).astype(np.int32)
+        path, idx = lib.walk(to_dev(edges), to_dev(cand))
+        torch.cuda.synchronize()
+        rpath, ridx, _, _ = ref.walk(edges, cand)   # same fp32 values: decisions must agree
+        assert_ids_equal(to_np(idx), ridx, "path_idx")
+        assert_ids_equal(to_np(path), rpath, "path")
+
+
+# ------------------------------------------------------------------------------- end to end
+
+def run_select(lib, x):
+    out = lib.select(to_dev(x.logits), to_dev(x.hidden), to_dev(x.W_sel), to_dev(x.pred_cb),
+                     to_dev(x.succ_cb), to_dev(x.anchor_ids), x.spec.k)
+    torch.cuda.synchronize()
+    return tuple(to_np(t) for t in out)
+
+
+@pytest.mark.parametrize("name", synth.CONFIG_ORDER)
+def test_select_workload(lib, ref, name):
+    x = synth.make_inputs(name)
+    s = x.spec
+    log(f"select {name}: B={s.B} L={s.L} k={s.k} V={s.V} H={s.H} r={s.r}")
+    gpu = run_select(lib, x)
+    want = ref.select(x.logits, x.hidden, x.W_sel, x.pred_cb, x.succ_cb, x.anchor_ids, s.k)
+    exempt = check_select(gpu, want)
+    log(f"  parity ok; near-tie steps exempt from the exact-path rule: {exempt} of {s.B * s.L}")
+
+
+SMALL_SELECT = [
+    # (B, L, V, H, r, k, logits, act, cb, recipe)
+    (1, 1, 1024, 64, 16, 4, "f32", "f32", "f32", "tiny"),
+    (3, 5, 1021, 100, 24, 7, "bf16", "bf16", "bf16", "normal"),
+    (2, 6, 4099, 64, 16, 64, "f32", "bf16", "f32", "normal"),
+    (4, 3, 300, 32, 8, 1, "bf16", "f32", "bf16", "normal"),
+    (2, 4, 50000, 256, 256, 16, "bf16", "bf16", "bf16", "normal"),
+    (3, 8, 2000, 64, 64, 32, "f32", "bf16", "bf16", "stress"),
+]
+
+
+@pytest.mark.parametrize("B,L,V,H,r,k,ld,ad,cd,recipe", SMALL_SELECT,
+                         ids=[f"B{c[0]}-L{c[1]}-V{c[2]}-H{c[3]}-r{c[4]}-k{c[5]}-{c[6]}{c[7]}{c[8]}-{c[9]}"
+                              for c in SMALL_SELECT])
+def test_select_shapes(lib, ref, B, L, V, H, r, k, ld, ad, cd, recipe):
+    s = synth.Spec("case", B, L, k, V, H, r, ld, ad, cd, recipe, 77)
+    log(f"select case {s}")
+    x = synth.make_inputs(s)
+    gpu = run_select(lib, x)
+    want = ref.select(x.logits, x.hidden, x.W_sel, x.pred_cb, x.succ_cb, x.anchor_ids, k)
+    check_select(gpu, want)
+
+
+def test_select_deterministic(lib):
+    x = synth.make_inputs("serving-b64")
+    a = run_select(lib, x)
+    b = run_select(lib, x)
+    for u, v, what in zip(a, b, ("cand_ids", "unary", "edges", "path")):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8)), f"{what} differs between runs"
+
+
+def test_select_reduces_to_argmax(lib):
+    x = synth.make_inputs(synth.spec("qwen3-8b-b1", B=2))
+    x.pred_cb[:] = 0
+    x.succ_cb[:] = 0
+    _, _, _, path = run_select(lib, x)
+    logits = synth.bf16_to_f32(x.logits)
+    assert np.array_equal(path, np.argmax(logits, axis=2))
+
+
+def test_select_exact_edge_tie(lib, ref):
+    # tokens 5 and 9 share the top logit and the successor code: exact edge ties in every row
+    s = synth.Spec("tie", 2, 3, 3, 64, 32, 8, "f32", "f32", "f32", "normal", 5)
+    x = synth.make_inputs(s)
+    x.logits[:, :, 5] = 20.0
+    x.logits[:, :, 9] = 20.0
+    x.succ_cb[9] = x.succ_cb[5]
+    cand, _, edges, path = run_select(lib, x)
+    assert np.array_equal(cand[:, :, :2], np.broadcast_to([5, 9], (2, 3, 2)))
+    assert np.all(edges[..., 0] == edges[..., 1])
+    assert np.all(path == 5)
+    want = ref.select(x.logits, x.hidden, x.W_sel, x.pred_cb, x.succ_cb, x.anchor_ids, 3)
+    check_path(path, cand, want.edges)
