@@ -1,0 +1,256 @@
+"""Benchmark of the DFlash 2 candidate selector on one MI355X.
+
+A step is one dflash2_select call: top-k + logsumexp, gate, lattice and walk over one batch of
+synthetic logits/hidden rows already resident in HBM. Logits and hidden rows rotate through a
+pool of copies larger than 1 GiB (over twice the 256 MB Infinity Cache), so every step streams
+its logits from HBM. The weights (W_sel, codebooks) are one copy, as in serving.
+
+Prints one JSON line:
+  value        selector positions/s = B*L*steps / elapsed (the default workload: serving-b64)
+  roofline     K1 (the top-k/logsumexp pass, the dominant kernel): algorithmic bytes per launch
+               (R*V*elem + R*k*8 + R*4) / mean K1 launch time (HIP events around a loop of K1-only
+               launches on the launch stream), against the MI355X HBM peak of 8 TB/s; `traffic`
+               comes from committed rocprofv3 counter readings when they match the current kernel
+  cpu_baseline the fp64 C oracle (single-threaded) on the host, on the same workload
+  per_config   end-to-end latency and K1 bandwidth of every workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "selector positions/sec and top-k pass HBM GB/s (% of peak) at V=151936, L=16, k=16"
+PEAK_HBM_GBS = 8000.0
+POOL_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "topk_lse_traffic.json")
+K1_SOURCE = os.path.join(ROOT, "dflash2_draft_candidate_amd", "csrc", "topk_lse.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def k1_bytes(s) -> int:
+    elem = 2 if s.logits_dtype == "bf16" else 4
+    return s.R * (s.V * elem + s.k * 8 + 4)
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+class Workload:
+    """Device-resident inputs for one workload, with a rotating pool of logits/hidden copies."""
+
+    def __init__(self, name: str, device: str):
+        import synth
+        import torch
+        t0 = time.time()
+        self.x = synth.make_inputs(name)
+        self.s = self.x.spec
+        t1 = time.time()
+        logits = synth.as_torch(self.x.logits, device)
+        hidden = synth.as_torch(self.x.hidden, device)
+        per = logits.numel() * logits.element_size() + hidden.numel() * hidden.element_size()
+        n = min(512, max(1, -(-POOL_BYTES // per)))
+        self.logits = [logits] + [logits.clone() for _ in range(n - 1)]
+        self.hidden = [hidden] + [hidden.clone() for _ in range(n - 1)]
+        self.W = synth.as_torch(self.x.W_sel, device)
+        self.pred = synth.as_torch(self.x.pred_cb, device)
+        self.succ = synth.as_torch(self.x.succ_cb, device)
+        self.anchor = synth.as_torch(self.x.anchor_ids, device)
+        s = self.s
+        self.out = (torch.empty((s.B, s.L, s.k), dtype=torch.int32, device=device),
+                    torch.empty((s.B, s.L, s.k), dtype=torch.float32, device=device),
+                    torch.empty((s.B, s.L, s.k, s.k), dtype=torch.float32, device=device),
+                    torch.empty((s.B, s.L), dtype=torch.int32, device=device))
+        import dflash2_draft_candidate_amd as d2
+        self.ws = torch.empty(max(16, d2.workspace_bytes(s.B, s.L, s.V, s.H, s.r, s.k)),
+                              dtype=torch.uint8, device=device)
+        torch.cuda.synchronize()
+        log(f"[bench] {name}: generated in {t1 - t0:.1f}s, pool of {n} logits/hidden copies")
+
+    def step(self, i: int):
+        import dflash2_draft_candidate_amd as d2
+        j = i % len(self.logits)
+        d2.select(self.logits[j], self.hidden[j], self.W, self.pred, self.succ, self.anchor,
+                  self.s.k, out=self.out, workspace=self.ws)
+
+    def k1_step(self, i: int, ids, unary, lse, ws):
+        import ctypes
+        import dflash2_draft_candidate_amd as d2
+        import torch
+        j = i % len(self.logits)
+        s = self.s
+        lg = self.logits[j]
+        rc = d2.library().dflash2_topk_lse(
+            ctypes.c_void_p(lg.data_ptr()), d2._dtype(lg), s.R, s.V, s.k,
+            ctypes.c_void_p(ids.data_ptr()), ctypes.c_void_p(unary.data_ptr()),
+            ctypes.c_void_p(lse.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"dflash2_topk_lse failed with status {rc}")
+
+
+def time_loop(fn, steps: int, warmup: int) -> float:
+    """Mean milliseconds per call of fn(i), HIP events on the current stream."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def measure(name: str, device: str, steps: int, warmup: int) -> dict:
+    import torch
+    w = Workload(name, device)
+    s = w.s
+    e2e_ms = time_loop(w.step, steps, warmup)
+    ids = torch.empty((s.R, s.k), dtype=torch.int32, device=device)
+    unary = torch.empty((s.R, s.k), dtype=torch.float32, device=device)
+    lse = torch.empty((s.R,), dtype=torch.float32, device=device)
+    import dflash2_draft_candidate_amd as d2
+    from dflash2_draft_candidate_amd import BF16, F32
+    wsb = d2.library().dflash2_topk_lse_workspace_bytes(s.R, s.V, s.k,
+                                                        BF16 if s.logits_dtype == "bf16" else F32)
+    ws = torch.empty(max(16, wsb), dtype=torch.uint8, device=device)
+    k1_ms = time_loop(lambda i: w.k1_step(i, ids, unary, lse, ws), steps, warmup)
+    gbs = k1_bytes(s) / (k1_ms * 1e-3) / 1e9
+    res = {"B": s.B, "L": s.L, "k": s.k, "V": s.V, "H": s.H, "r": s.r,
+           "logits": s.logits_dtype, "e2e_us": round(e2e_ms * 1e3, 2),
+           "positions_per_s": round(s.R / (e2e_ms * 1e-3), 1), "k1_us": round(k1_ms * 1e3, 2),
+           "k1_gbs": round(gbs, 1), "k1_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    res["_workload"] = w
+    return res
+
+
+def cpu_baseline(name: str, min_seconds: float = 10.0, max_passes: int = 8) -> dict:
+    """The oracle (fp64 C, one thread) on the host over whole passes of the workload."""
+    import oracle
+    import synth
+    x = synth.make_inputs(name)
+    o = oracle.default()
+    passes, elapsed = 0, 0.0
+    while passes < max_passes and (passes == 0 or elapsed < min_seconds):
+        t0 = time.perf_counter()
+        o.select(x.logits, x.hidden, x.W_sel, x.pred_cb, x.succ_cb, x.anchor_ids, x.spec.k)
+        elapsed += time.perf_counter() - t0
+        passes += 1
+    R = x.spec.R
+    return {"value": round(R * passes / elapsed, 1), "unit": "positions/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{passes} full pass(es) of the {name} workload ({R} positions each), "
+                      f"{elapsed:.1f} s total, single-threaded fp64 C"}
+
+
+def committed_traffic() -> dict | None:
+    """HBM bytes per K1 launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE readings, if they
+    were taken on the current K1 source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("k1_source_sha256_16") != source_hash(K1_SOURCE):
+        return None
+    return t
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="serving-b64")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true")
+    ap.add_argument("--k1-only", action="store_true",
+                    help="only loop K1 launches (for counter collection), no JSON")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each sequence is "
+              "independent; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dflash2_draft_candidate_amd  # noqa: F401  fails loudly if the library is not built
+    import synth
+    device = "cuda:0"
+    torch.cuda.set_device(0)
+
+    if args.k1_only:
+        w = Workload(args.workload, device)
+        s = w.s
+        ids = torch.empty((s.R, s.k), dtype=torch.int32, device=device)
+        unary = torch.empty((s.R, s.k), dtype=torch.float32, device=device)
+        lse = torch.empty((s.R,), dtype=torch.float32, device=device)
+        import dflash2_draft_candidate_amd as d2
+        wsb = d2.library().dflash2_topk_lse_workspace_bytes(
+            s.R, s.V, s.k, d2.BF16 if s.logits_dtype == "bf16" else d2.F32)
+        ws = torch.empty(max(16, wsb), dtype=torch.uint8, device=device)
+        ms = time_loop(lambda i: w.k1_step(i, ids, unary, lse, ws), args.steps, args.warmup)
+        log(f"[bench] k1-only {args.workload}: {ms * 1e3:.2f} us/launch, "
+            f"{k1_bytes(s) / (ms * 1e-3) / 1e9:.1f} GB/s")
+        return
+
+    main_res = measure(args.workload, device, args.steps, args.warmup)
+    s = main_res.pop("_workload").s
+    log(f"[bench] {args.workload}: {main_res}")
+    per_config = {args.workload: main_res}
+    if not args.no_per_config:
+        for name in synth.CONFIG_ORDER:
+            if name == args.workload:
+                continue
+            r = measure(name, device, args.steps, args.warmup)
+            r.pop("_workload")
+            torch.cuda.empty_cache()
+            per_config[name] = r
+            log(f"[bench] {name}: {r}")
+
+    traffic = committed_traffic()
+    roof = {"bound": "hbm", "achieved": main_res["k1_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": main_res["k1_frac"],
+            "traffic": traffic["bytes_per_launch"] if traffic and
+            traffic.get("workload") == args.workload else None,
+            "kernel": "topk_lse_kernel", "algorithmic_bytes_per_launch": k1_bytes(s),
+            "launch_us": main_res["k1_us"]}
+    line = {
+        "metric": METRIC,
+        "value": main_res["positions_per_s"],
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["e2e_us"] / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": s.B, "L": s.L, "k": s.k, "V": s.V, "H": s.H,
+                   "r": s.r, "logits_dtype": s.logits_dtype, "act_dtype": s.act_dtype,
+                   "codebook_dtype": s.cb_dtype, "global_batch": s.B, "seq_len": s.L,
+                   "parallelism": "single-gpu"},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.workload)
+    line["per_config"] = per_config
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
