@@ -37,21 +37,19 @@ int check_ptrs(std::initializer_list<const void *> ptrs) {
 int64_t rows_of(int B, int L) { return (int64_t)B * L; }
 
 struct SelectLayout {
-    size_t lse, g, topk, gate, total;
+    size_t lse, gpart, topk, total;
 };
 
-// Workspace of dflash2_select for one logits dtype: lse [R] | g [R, r] | K1 partials | K2 partials.
-SelectLayout select_layout(int R, int V, int H, int r, int logits_dtype) {
+// Workspace of dflash2_select: lse [R] | gate partials [splits][R][r] | K1 slice partials.
+SelectLayout select_layout(int R, int V, int H, int r, int logits_dtype, int act_dtype) {
     SelectLayout s;
     size_t off = 0;
     s.lse = off;
     off += round_up((size_t)R * sizeof(float));
-    s.g = off;
-    off += round_up((size_t)R * r * sizeof(float));
+    s.gpart = off;
+    off += round_up((size_t)gate_splits(R, H, act_dtype) * R * r * sizeof(float));
     s.topk = off;
     off += round_up(topk_workspace_bytes(plan_topk(R, V, logits_dtype == DFLASH2_F32 ? 4 : 2), R));
-    s.gate = off;
-    off += round_up(gate_workspace_bytes(plan_gate(R, H, r), R, r));
     s.total = off;
     return s;
 }
@@ -99,7 +97,7 @@ int dflash2_topk_lse(const void *logits, int logits_dtype, int R, int V, int k, 
 
 size_t dflash2_gate_workspace_bytes(int R, int H, int r) {
     if (R < 1 || H < 1 || r < 1 || r > DFLASH2_MAX_R) return 0;
-    return gate_workspace_bytes(plan_gate(R, H, r), R, r);
+    return gate_workspace_bytes(R, H, r, DFLASH2_BF16);
 }
 
 int dflash2_gate(const void *hidden, const void *W_sel, int act_dtype, int R, int H, int r,
@@ -126,8 +124,8 @@ int dflash2_lattice(const int32_t *cand_ids, const float *unary, const float *g,
         return DFLASH2_ERR_INVALID_ARG;
     int rc = check_ptrs({cand_ids, unary, g, pred_cb, succ_cb, anchor_ids, edges});
     if (rc) return rc;
-    return hip_status(launch_lattice(cand_ids, unary, g, pred_cb, succ_cb, cb_dtype, anchor_ids, B,
-                                     L, V, r, k, edges, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_lattice(cand_ids, unary, g, 1, pred_cb, succ_cb, cb_dtype, anchor_ids,
+                                     B, L, V, r, k, edges, static_cast<hipStream_t>(stream)));
 }
 
 int dflash2_walk(const float *edges, const int32_t *cand_ids, int B, int L, int k, int32_t *path,
@@ -146,9 +144,13 @@ size_t dflash2_workspace_bytes(int B, int L, int V, int H, int r, int k) {
         check_rows((int)rows_of(B, L), V, k) != DFLASH2_OK)
         return 0;
     const int R = (int)rows_of(B, L);
-    const size_t a = select_layout(R, V, H, r, DFLASH2_F32).total;
-    const size_t b = select_layout(R, V, H, r, DFLASH2_BF16).total;
-    return a > b ? a : b;
+    size_t most = 0;
+    for (int ld = DFLASH2_F32; ld <= DFLASH2_BF16; ++ld)
+        for (int ad = DFLASH2_F32; ad <= DFLASH2_BF16; ++ad) {
+            const size_t t = select_layout(R, V, H, r, ld, ad).total;
+            most = t > most ? t : most;
+        }
+    return most;
 }
 
 int dflash2_select(const void *logits, int logits_dtype, const void *hidden, int act_dtype,
@@ -170,18 +172,19 @@ int dflash2_select(const void *logits, int logits_dtype, const void *hidden, int
     if (!workspace || workspace_bytes < need) return DFLASH2_ERR_WORKSPACE;
     if (!aligned16(workspace)) return DFLASH2_ERR_ALIGNMENT;
 
-    const SelectLayout lay = select_layout(R, V, H, r, logits_dtype);
+    const SelectLayout lay = select_layout(R, V, H, r, logits_dtype, act_dtype);
     char *ws = static_cast<char *>(workspace);
     float *lse = reinterpret_cast<float *>(ws + lay.lse);
-    float *g = reinterpret_cast<float *>(ws + lay.g);
+    float *gpart = reinterpret_cast<float *>(ws + lay.gpart);
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     hipError_t e = launch_topk_lse(logits, logits_dtype, R, V, k, cand_ids, unary, lse,
                                    ws + lay.topk, s);
-    if (e == hipSuccess) e = launch_gate(hidden, W_sel, act_dtype, R, H, r, g, ws + lay.gate, s);
     if (e == hipSuccess)
-        e = launch_lattice(cand_ids, unary, g, pred_cb, succ_cb, cb_dtype, anchor_ids, B, L, V, r,
-                           k, edges, s);
+        e = launch_gate_partials(hidden, W_sel, act_dtype, R, H, r, gpart, s);
+    if (e == hipSuccess)
+        e = launch_lattice(cand_ids, unary, gpart, gate_splits(R, H, act_dtype), pred_cb, succ_cb,
+                           cb_dtype, anchor_ids, B, L, V, r, k, edges, s);
     if (e == hipSuccess) e = launch_walk(edges, cand_ids, B, L, k, path, nullptr, s);
     return hip_status(e);
 }

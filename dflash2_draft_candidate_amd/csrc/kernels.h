@@ -19,17 +19,20 @@ hipError_t launch_topk_lse(const void *logits, int logits_dtype, int R, int V, i
                            hipStream_t stream);
 
 // ---- K2: gate GEMM ---------------------------------------------------------------------------
-struct GatePlan {
-    int ksplit;  // workgroups along H; > 1 adds a reduction kernel and needs workspace
-};
-GatePlan plan_gate(int R, int H, int r);
-size_t gate_workspace_bytes(const GatePlan &plan, int R, int r);
+// bf16 runs as `gate_splits` partial products over ranges of H, [splits][R][r] floats;
+// fp32 runs as one split. launch_gate_partials writes the partials (one split = g itself);
+// launch_gate also sums them into g (workspace: gate_workspace_bytes).
+int gate_splits(int R, int H, int act_dtype);
+size_t gate_workspace_bytes(int R, int H, int r, int act_dtype);
+hipError_t launch_gate_partials(const void *hidden, const void *W_sel, int act_dtype, int R,
+                                int H, int r, float *part, hipStream_t stream);
 hipError_t launch_gate(const void *hidden, const void *W_sel, int act_dtype, int R, int H, int r,
                        float *g, void *workspace, hipStream_t stream);
 
 // ---- K3: lattice -----------------------------------------------------------------------------
-hipError_t launch_lattice(const int32_t *cand_ids, const float *unary, const float *g,
-                          const void *pred_cb, const void *succ_cb, int cb_dtype,
+// gpart: the gate as `ksplit` partial rows [ksplit][B*L][r], summed in split order.
+hipError_t launch_lattice(const int32_t *cand_ids, const float *unary, const float *gpart,
+                          int ksplit, const void *pred_cb, const void *succ_cb, int cb_dtype,
                           const int32_t *anchor_ids, int B, int L, int V, int r, int k,
                           float *edges, hipStream_t stream);
 

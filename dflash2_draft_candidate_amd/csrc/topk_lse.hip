@@ -107,9 +107,47 @@ __device__ __forceinline__ u32x4 load_vec(const T *base, int64_t vec) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base) + vec);
 }
 
+template <typename T, int U>
+__device__ __forceinline__ void load_batch(const T *logits, int64_t vbase, int lane, u32x4 *buf) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) buf[u] = load_vec(logits, vbase + lane + u * kWave);
+}
+
+// One full batch: U vectors per lane starting at vector vbase (+ lane + u * 64), all in the row.
+template <typename T, int U, bool SEED>
+__device__ __forceinline__ void full_batch(const u32x4 *buf, int64_t vbase, int64_t g0, int k,
+                                           WaveTopk &w, float &ref, float &sum, int lane) {
+    constexpr int EV = Elem<T>::kPerVec;
+    constexpr int NB = U * EV;
+    float x[NB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) Elem<T>::unpack(buf[u], x + u * EV);
+    float bmax = x[0];
+#pragma unroll
+    for (int j = 1; j < NB; ++j) bmax = fmaxf(bmax, x[j]);
+    lse_update_full<NB>(ref, sum, x, bmax);
+    if (SEED) {
+        // Threshold seed: the k-th largest lane maximum (k real elements reach it).
+        const uint64_t lk = wave_sort_desc((uint64_t)value_key(bmax) << 32, lane);
+        w.tau_key = __shfl(lk, k - 1, kWave);
+        w.tau_v = key_logit(w.tau_key);
+    }
+    int32_t id[NB];
+    bool valid[NB];
+    const int32_t id0 = (int32_t)((vbase + lane) * EV - g0);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < EV; ++e) {
+            id[u * EV + e] = id0 + u * kWave * EV + e;
+            valid[u * EV + e] = true;
+        }
+    offer<NB>(w, x, id, valid, bmax, lane);
+}
+
 // Elements [e0, e1) of the flat tensor, one per lane per step (ragged row ends).
 template <typename T>
-__device__ void scalar_range(const T *logits, int64_t e0, int64_t e1, int64_t row_start,
+__device__ __forceinline__ void scalar_range(const T *logits, int64_t e0, int64_t e1, int64_t row_start,
                              WaveTopk &w, float &ref, float &sum, int lane) {
     for (int64_t e = e0; e < e1; e += kWave) {
         const int64_t ei = e + lane;
@@ -154,37 +192,23 @@ __global__ __launch_bounds__(WAVES * kWave) void topk_lse_kernel(
     w.k = k;
     float ref = -INFINITY, sum = 0.0f;
 
-    int64_t vbase = c0;
-    bool first = true;
-    for (; vbase + (int64_t)U * kWave <= c1; vbase += (int64_t)U * kWave) {
-        u32x4 raw[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) raw[u] = load_vec(logits, vbase + lane + u * kWave);
-        float x[NB];
-#pragma unroll
-        for (int u = 0; u < U; ++u) Elem<T>::unpack(raw[u], x + u * EV);
-        float bmax = x[0];
-#pragma unroll
-        for (int j = 1; j < NB; ++j) bmax = fmaxf(bmax, x[j]);
-        lse_update_full<NB>(ref, sum, x, bmax);
-        if (first) {
-            // Seed the threshold: the k-th largest lane maximum (k real elements reach it).
-            const uint64_t lk = wave_sort_desc((uint64_t)value_key(bmax) << 32, lane);
-            w.tau_key = __shfl(lk, k - 1, kWave);
-            w.tau_v = key_logit(w.tau_key);
-            first = false;
+    // Full batches (U vectors per lane), double-buffered: the next batch is in flight while the
+    // current one is processed. The first batch also seeds the threshold.
+    const int64_t step = (int64_t)U * kWave;
+    const int64_t nfull = (c1 - c0) / step;
+    int64_t vbase = c0 + nfull * step;
+    if (nfull > 0) {
+        u32x4 bufA[U], bufB[U];
+        load_batch<T, U>(logits, c0, lane, bufA);
+        if (nfull > 1) load_batch<T, U>(logits, c0 + step, lane, bufB);
+        full_batch<T, U, true>(bufA, c0, g0, k, w, ref, sum, lane);
+        for (int64_t b = 1; b < nfull; b += 2) {
+            if (b + 1 < nfull) load_batch<T, U>(logits, c0 + (b + 1) * step, lane, bufA);
+            full_batch<T, U, false>(bufB, c0 + b * step, g0, k, w, ref, sum, lane);
+            if (b + 1 >= nfull) break;
+            if (b + 2 < nfull) load_batch<T, U>(logits, c0 + (b + 2) * step, lane, bufB);
+            full_batch<T, U, false>(bufA, c0 + (b + 1) * step, g0, k, w, ref, sum, lane);
         }
-        int32_t id[NB];
-        bool valid[NB];
-        const int32_t id0 = (int32_t)((vbase + lane) * EV - g0);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int e = 0; e < EV; ++e) {
-                id[u * EV + e] = id0 + u * kWave * EV + e;
-                valid[u * EV + e] = true;
-            }
-        offer<NB>(w, x, id, valid, bmax, lane);
     }
     // Remaining vectors: one per lane per step.
     for (; vbase < c1; vbase += kWave) {

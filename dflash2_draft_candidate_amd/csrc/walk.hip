@@ -7,9 +7,11 @@
 // "What llama.cpp Actually Builds for the Selector" (the runtime walk: predecessor = anchor, best
 // successor per position, emit the chosen token).
 //
-// One workgroup per sequence. The lattice is staged into LDS a chunk of positions at a time
-// (coalesced, all 4 waves), then wave 0 walks it: lane j holds edge j of the current row and a
-// 6-step butterfly finds the (value, lowest index) maximum.
+// The walk only ever needs, for each position p and predecessor i, the best successor
+// best[p][i] = argmax_j edges[b][p][i][j]; all of those are independent. So one workgroup per
+// sequence stages a chunk of positions (edges and candidate ids) in LDS with coalesced loads,
+// computes every best[p][i] in parallel (one row per thread), and only the final pointer chase
+// j_p = best[p][j_{p-1}] is sequential: one LDS read per position.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -24,39 +26,87 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(const float *__restr
                                                             int L, int k,
                                                             int32_t *__restrict__ path,
                                                             int32_t *__restrict__ path_idx) {
-    __shared__ float E[kWalkLds];
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    __shared__ __attribute__((aligned(16))) float E[kWalkLds];
+    __shared__ int32_t C[kWalkLds / 2];
+    __shared__ int32_t best[kWalkLds / 2];
+    const int tid = threadIdx.x;
     const int64_t b = blockIdx.x;
     const int per_pos = k * k;
-    const int chunk = kWalkLds / per_pos;  // >= 2 for k <= 64
+    const int chunk = min(kWalkLds / per_pos, (kWalkLds / 2) / k);  // >= 2 for k <= 64
     int prev = 0;
     for (int p0 = 0; p0 < L; p0 += chunk) {
         const int np = min(chunk, L - p0);
         __syncthreads();
-        const float *src = edges + (b * L + p0) * per_pos;
-        for (int e = tid; e < np * per_pos; e += kWalkThreads) E[e] = src[e];
-        __syncthreads();
-        if (wave != 0) continue;
-        for (int q = 0; q < np; ++q) {
-            float v = lane < k ? E[q * per_pos + prev * k + lane] : -INFINITY;
-            int j = lane;
+        const int64_t row0 = b * L + p0;
+        const float *src = edges + row0 * per_pos;
+        const int ne = np * per_pos;
+        // Staging loads are issued in batches of 8 per thread before any LDS store, so they are
+        // in flight together (at most 8192 floats: 8 float4 per thread).
+        if (((row0 * per_pos) & 3) == 0 && (ne & 3) == 0) {  // 16-byte aligned run
+            const float4 *s4 = reinterpret_cast<const float4 *>(src);
+            float4 *e4 = reinterpret_cast<float4 *>(E);
+            float4 t[8];
 #pragma unroll
-            for (int off = kWave / 2; off > 0; off >>= 1) {
-                const float ov = __shfl_xor(v, off, kWave);
-                const int oj = __shfl_xor(j, off, kWave);
-                if (ov > v || (ov == v && oj < j)) {
-                    v = ov;
-                    j = oj;
+            for (int u = 0; u < 8; ++u) {
+                const int e = tid + u * kWalkThreads;
+                t[u] = s4[e < ne / 4 ? e : 0];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int e = tid + u * kWalkThreads;
+                if (e < ne / 4) e4[e] = t[u];
+            }
+        } else {
+            for (int e0 = 0; e0 < ne; e0 += 8 * kWalkThreads) {
+                float t[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int e = e0 + tid + u * kWalkThreads;
+                    t[u] = src[e < ne ? e : 0];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int e = e0 + tid + u * kWalkThreads;
+                    if (e < ne) E[e] = t[u];
                 }
             }
-            j = __builtin_amdgcn_readfirstlane(j);
-            j = j < k ? j : k - 1;
-            const int64_t row = b * L + p0 + q;
-            if (lane == 0) {
-                path[row] = cand_ids[row * k + j];
-                if (path_idx) path_idx[row] = j;
+        }
+        for (int e0 = 0; e0 < np * k; e0 += 4 * kWalkThreads) {
+            int32_t t[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + tid + u * kWalkThreads;
+                t[u] = cand_ids[row0 * k + (e < np * k ? e : 0)];
             }
-            prev = j;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + tid + u * kWalkThreads;
+                if (e < np * k) C[e] = t[u];
+            }
+        }
+        __syncthreads();
+        // best successor of every (position, predecessor) row: lowest index among the maxima
+        for (int t = tid; t < np * k; t += kWalkThreads) {
+            const float *rowp = E + t * k;
+            float bv = rowp[0];
+            int bj = 0;
+            for (int j = 1; j < k; ++j) {
+                const float v = rowp[j];
+                if (v > bv) {
+                    bv = v;
+                    bj = j;
+                }
+            }
+            best[t] = bj;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            for (int q = 0; q < np; ++q) {
+                const int j = best[q * k + prev];
+                path[row0 + q] = C[q * k + j];
+                if (path_idx) path_idx[row0 + q] = j;
+                prev = j;
+            }
         }
     }
 }
