@@ -23,6 +23,12 @@ template <typename T> struct Elem;
 template <> struct Elem<float> {
     static constexpr int kPerVec = 4;  // elements per 16-byte vector
     static __device__ __forceinline__ float load(const float *p, int64_t i) { return p[i]; }
+    // element i of vectors staged in LDS
+    static __device__ __forceinline__ float lds_element(const u32x4 *v, int i) {
+        return reinterpret_cast<const float *>(v)[i];
+    }
+    // a vector whose element 0 is x
+    static __device__ __forceinline__ u32x4 single(float x) { return u32x4{__float_as_uint(x), 0u, 0u, 0u}; }
     static __device__ __forceinline__ void unpack(const u32x4 &v, float *x) {
         x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
         x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
@@ -31,6 +37,11 @@ template <> struct Elem<float> {
 template <> struct Elem<uint16_t> {
     static constexpr int kPerVec = 8;
     static __device__ __forceinline__ float load(const uint16_t *p, int64_t i) { return bf16_to_f32(p[i]); }
+    static __device__ __forceinline__ float lds_element(const u32x4 *v, int i) {
+        return bf16_to_f32(reinterpret_cast<const uint16_t *>(v)[i]);
+    }
+    // x came from a bf16 value, so its upper half is exact
+    static __device__ __forceinline__ u32x4 single(float x) { return u32x4{__float_as_uint(x) >> 16, 0u, 0u, 0u}; }
     static __device__ __forceinline__ void unpack(const u32x4 &v, float *x) {
         x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
         x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);

@@ -22,7 +22,8 @@ int hip_status(hipError_t e) { return e == hipSuccess ? DFLASH2_OK : DFLASH2_ERR
 
 // Sizes shared by select and its stages; 0 = valid.
 int check_rows(int R, int V, int k) {
-    if (R < 1 || V < 1 || k < 1 || k > DFLASH2_MAX_K || k > V) return DFLASH2_ERR_INVALID_ARG;
+    if (R < 1 || V < 1 || V > DFLASH2_MAX_V || k < 1 || k > DFLASH2_MAX_K || k > V)
+        return DFLASH2_ERR_INVALID_ARG;
     return DFLASH2_OK;
 }
 

@@ -122,7 +122,8 @@ __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
     constexpr int D = batch_steps<NT>();
     __shared__ float red[kGateWaves][16][NC + (NT == 16 ? 0 : 1)];  // <= 64 KB
 
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int m = lane & 15, g = lane >> 4;
     const int row = blockIdx.x * 16 + m;
     const bool row_ok = row < R;

@@ -6,82 +6,144 @@
 // (top 16 candidates per position; unary term U_t(b)); "DFlash2 Lands in llama.cpp" (ramgpt.org),
 // section "What llama.cpp Actually Builds for the Selector" (per-position top-k, gathered unary).
 //
-// Design (gfx950, wave64):
-//   * A row is cut into S slices (one workgroup each) and each slice into one contiguous range
-//     per wave. Lanes read 16-byte vectors, consecutive lanes consecutive vectors (coalesced),
-//     U vectors in flight per lane.
-//   * logsumexp: each lane keeps an online (ref, sum) pair in the log2 domain; one v_exp per
+// Design (gfx950, wave64): a workgroup of W waves per (row, slice); each wave streams its own
+// contiguous part of the row. W is chosen so that about 16 waves share a CU (4 per SIMD): the
+// SIMD then overlaps one wave's arithmetic with the other waves' loads. A row has S slices
+// (S = 1 unless rows are too few to fill the chip; the slices are merged by a second kernel in
+// slice order).
+//   * Streaming: lanes read 16-byte vectors (consecutive lanes consecutive vectors) through a
+//     buffer descriptor bounded to the wave's range, U vectors per lane per batch, NBUF - 1
+//     batches issued ahead of the one processed.
+//   * logsumexp: each lane keeps an online (ref, sum) pair in the log2 domain: one v_exp per
 //     element plus one rescale per batch.
 //   * top-k: each wave keeps its 64 best keys sorted across its lanes (lane = rank). An element
-//     is a candidate only if it beats the wave's current k-th key; the rare candidates are
-//     compacted into a per-wave LDS staging list with ballot + popcount and merged into the
-//     sorted list 64 at a time by a bitonic sort + merge across the lanes. The first full batch
-//     seeds the threshold with the k-th largest of the 64 lane maxima (k real elements are at or
-//     above it), so almost nothing is staged after the first batch.
-//   * The waves' lists and (ref, sum) pairs are merged in fixed order: the result is
-//     deterministic. With S > 1 a second kernel merges the slices in slice order.
+//     is admitted only if it beats the workgroup threshold: the largest k-th key any wave of the
+//     workgroup holds, shared through LDS (each such key has k keys at or above it, so nothing
+//     below it can be in the row's top k). A batch costs one compare per lane when no lane beats
+//     it. Otherwise the lanes that do publish their raw batch to LDS and the wave reads each such
+//     lane's elements back transposed (lane j <- element j). Each candidate is inserted straight
+//     into the sorted list (rank by ballot + popcount, a one-lane DPP shift), and the wave's
+//     k-th key is read back with readlane.
+//   * The threshold starts at the k-th largest of the 64 lane maxima of each wave's first batch
+//     (k real elements reach it).
+//   * The waves' lists and (ref, sum) pairs are merged in wave order at the end.
+// All orders are fixed and the merged top-k of distinct keys is unique, so results are
+// deterministic.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace dflash2 {
 namespace {
 
-constexpr int kStageCap = 2 * kWave;  // staging list capacity per wave (keys)
+constexpr int kU = 4;     // 16-byte vectors per lane per batch
+constexpr int kRing = 3;  // batches in flight per wave (kRing - 1 ahead of the one processed)
+constexpr int kMaxWaves = 8;              // waves per workgroup (LDS: 4 KB each)
+constexpr int kBufferWord3 = 0x00020000;  // gfx9-family buffer descriptor word 3 (raw data)
+constexpr int kNonTemporal = 2;           // cache policy: streaming data, read once
+constexpr int kDppWaveShr1 = 0x138;       // DPP control: lane i reads lane i - 1
+
+// Wave-uniform 64-bit broadcast of lane `src` (src uniform): two v_readlane, no LDS round trip.
+__device__ __forceinline__ uint64_t lane_value(uint64_t v, int src) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, src);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), src);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Lane i receives lane i - 1's value (lane 0 receives 0).
+__device__ __forceinline__ uint64_t shift_up_one(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, kDppWaveShr1, 0xF, 0xF, false);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), kDppWaveShr1, 0xF,
+                                                    0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
 
 struct WaveTopk {
     uint64_t top;      // this lane's entry of the wave's sorted list (lane = rank)
     uint64_t tau_key;  // admission threshold (wave-uniform): a key must exceed it
     float tau_v;       // logit of the threshold, for the cheap first test
-    int cnt;           // staged keys (wave-uniform)
-    uint64_t *stage;   // LDS [kStageCap]
     int k;
+    uint64_t *shared_tau;  // the workgroup threshold in LDS
 };
 
-__device__ __forceinline__ void wave_flush(WaveTopk &w, int lane) {
-    uint64_t c = lane < w.cnt ? w.stage[lane] : 0ull;
-    c = wave_sort_desc(c, lane);
-    w.top = wave_merge_desc(w.top, c, lane);
-    const int rest = w.cnt - kWave;
-    if (rest > 0) {
-        const uint64_t t = lane < rest ? w.stage[kWave + lane] : 0ull;
-        if (lane < rest) w.stage[lane] = t;
-    }
-    w.cnt = rest > 0 ? rest : 0;
-    const uint64_t kth = __shfl(w.top, w.k - 1, kWave);
-    if (kth != 0ull) {
-        w.tau_key = kth;
-        w.tau_v = key_logit(kth);
+__device__ __forceinline__ void set_tau(WaveTopk &w, uint64_t key) {
+    w.tau_key = key;
+    w.tau_v = key_logit(key);
+}
+
+// The wave's own k-th key rose to `key`: adopt it and publish it to the workgroup.
+__device__ __forceinline__ void raise_tau(WaveTopk &w, uint64_t key, int lane) {
+    if (key > w.tau_key) {
+        set_tau(w, key);
+        if (lane == 0)
+            __hip_atomic_fetch_max(w.shared_tau, key, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
     }
 }
 
-// Stage `key` from every lane where `hit` holds; flush once 64 or more are staged.
-__device__ __forceinline__ void wave_stage(WaveTopk &w, bool hit, uint64_t key, int lane) {
-    const uint64_t mask = __ballot(hit);
-    if (mask == 0ull) return;
-    const int pos = w.cnt + __popcll(mask & ((1ull << lane) - 1ull));
-    if (hit) w.stage[pos] = key;
-    w.cnt += __popcll(mask);
-    if (w.cnt >= kWave) wave_flush(w, lane);
+// Adopt the workgroup threshold if another wave has raised it past ours.
+__device__ __forceinline__ void pull_tau(WaveTopk &w) {
+    const uint64_t s = __hip_atomic_load(w.shared_tau, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_WORKGROUP);
+    // readfirstlane returns int: widen through uint32_t (no sign extension into the high half)
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)s);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(s >> 32));
+    const uint64_t su = ((uint64_t)hi << 32) | lo;
+    if (su > w.tau_key) set_tau(w, su);
 }
 
-// Offer NB elements per lane (ids id[j]) to the wave's top-k. `valid` masks padding lanes.
-template <int NB>
-__device__ __forceinline__ void offer(WaveTopk &w, const float *x, const int32_t *id,
-                                      const bool *valid, float lane_max, int lane) {
-    if (__ballot(lane_max >= w.tau_v) == 0ull) return;
+// Insert key c (wave-uniform, above the threshold) into the sorted list: its rank is the number
+// of larger entries (a ballot), entries from that rank on move down one lane, and the threshold
+// follows the wave's k-th key once k entries exist.
+__device__ __forceinline__ void wave_insert(WaveTopk &w, uint64_t c, int lane) {
+    const int p = __popcll(__ballot(w.top > c));
+    const uint64_t prev = shift_up_one(w.top);
+    w.top = lane < p ? w.top : (lane == p ? c : prev);
+    raise_tau(w, lane_value(w.top, w.k - 1), lane);
+}
+
+// Offer a batch to the wave's top-k. Each lane holds U raw 16-byte vectors in `buf`, of which
+// the first NSLOT elements are used; element j of lane L is real only if its vector
+// (j / EV) * 64 + L is below `nvalid` (the raw words of the others may hold anything).
+// `lane_max` is the largest real element of the lane. Element j of lane L has id
+// id_base + L * lane_stride + (j / EV) * 64 * EV + (j % EV).
+template <typename T, int U, int NSLOT>
+__device__ __forceinline__ void offer_lanes(WaveTopk &w, const u32x4 *buf, float lane_max,
+                                            bool lane_ok, int nvalid, int32_t id_base,
+                                            int lane_stride, int lane, u32x4 *xbuf) {
+    constexpr int EV = Elem<T>::kPerVec;
+    static_assert(NSLOT <= kWave && NSLOT <= U * EV, "one element per lane in the transpose");
+    const bool mine = lane_ok && lane_max >= w.tau_v;
+    uint64_t hits = __ballot(mine);
+    if (hits == 0ull) return;
+    if (mine) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-        const bool maybe = valid[j] && x[j] >= w.tau_v;
+        for (int u = 0; u < U; ++u) xbuf[lane * U + u] = buf[u];
+    }
+    const int j = lane;  // this lane reads element j of each publishing lane
+    const int32_t id_j = (j / EV) * kWave * EV + (j % EV);
+    const int vec_j = (j / EV) * kWave;
+    while (hits != 0ull) {
+        const int L = __builtin_ctzll(hits);
+        hits &= hits - 1ull;
+        float x = -INFINITY;
+        if (j < NSLOT) x = Elem<T>::lds_element(xbuf, L * U * EV + j);
+        const bool maybe = j < NSLOT && vec_j + L < nvalid && x >= w.tau_v && x != -INFINITY;
         if (__ballot(maybe) != 0ull) {
-            const uint64_t key = cand_key(x[j], id[j]);
-            wave_stage(w, maybe && key > w.tau_key, key, lane);
+            const uint64_t key = cand_key(x, id_base + L * lane_stride + id_j);
+            uint64_t m = __ballot(maybe && key > w.tau_key);
+            while (m != 0ull) {
+                const int src = __builtin_ctzll(m);
+                m &= m - 1ull;
+                const uint64_t c = lane_value(key, src);
+                if (c > w.tau_key) wave_insert(w, c, lane);
+            }
         }
     }
 }
 
-// One lane's online logsumexp update with NB elements, all valid.
+// One lane's online logsumexp update with NB elements (-inf elements add nothing).
 template <int NB>
-__device__ __forceinline__ void lse_update_full(float &ref, float &sum, const float *x, float bmax) {
+__device__ __forceinline__ void lse_update(float &ref, float &sum, const float *x, float bmax) {
     const float r = fmaxf(ref, bmax * kLog2e);
     sum *= __builtin_amdgcn_exp2f(ref - r);  // ref = -inf on the first batch: factor 0
     ref = r;
@@ -89,151 +151,178 @@ __device__ __forceinline__ void lse_update_full(float &ref, float &sum, const fl
     for (int j = 0; j < NB; ++j) sum += __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -r));
 }
 
-// Same with per-element validity (padding lanes and ragged ends).
-template <int NB>
-__device__ __forceinline__ void lse_update_masked(float &ref, float &sum, const float *x,
-                                                  const bool *valid, float bmax) {
-    if (bmax == -INFINITY) return;  // no valid element in this lane
-    const float r = fmaxf(ref, bmax * kLog2e);
+// One element, possibly absent (ragged ends and idle lanes).
+__device__ __forceinline__ void lse_update_one(float &ref, float &sum, float x, bool valid) {
+    if (!valid) return;
+    const float r = fmaxf(ref, x * kLog2e);
     if (ref != r) sum *= __builtin_amdgcn_exp2f(ref - r);
     ref = r;
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-        if (valid[j]) sum += __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -r));
+    sum += __builtin_amdgcn_exp2f(fmaf(x, kLog2e, -r));
 }
 
-template <typename T>
-__device__ __forceinline__ u32x4 load_vec(const T *base, int64_t vec) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base) + vec);
-}
-
-template <typename T, int U>
-__device__ __forceinline__ void load_batch(const T *logits, int64_t vbase, int lane, u32x4 *buf) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) buf[u] = load_vec(logits, vbase + lane + u * kWave);
-}
-
-// One full batch: U vectors per lane starting at vector vbase (+ lane + u * 64), all in the row.
-template <typename T, int U, bool SEED>
-__device__ __forceinline__ void full_batch(const u32x4 *buf, int64_t vbase, int64_t g0, int k,
-                                           WaveTopk &w, float &ref, float &sum, int lane) {
-    constexpr int EV = Elem<T>::kPerVec;
-    constexpr int NB = U * EV;
-    float x[NB];
-#pragma unroll
-    for (int u = 0; u < U; ++u) Elem<T>::unpack(buf[u], x + u * EV);
-    float bmax = x[0];
-#pragma unroll
-    for (int j = 1; j < NB; ++j) bmax = fmaxf(bmax, x[j]);
-    lse_update_full<NB>(ref, sum, x, bmax);
-    if (SEED) {
-        // Threshold seed: the k-th largest lane maximum (k real elements reach it).
-        const uint64_t lk = wave_sort_desc((uint64_t)value_key(bmax) << 32, lane);
-        w.tau_key = __shfl(lk, k - 1, kWave);
-        w.tau_v = key_logit(w.tau_key);
-    }
-    int32_t id[NB];
-    bool valid[NB];
-    const int32_t id0 = (int32_t)((vbase + lane) * EV - g0);
+// U vectors of batch `b`: lane offset `voff` (fixed per lane) plus the wave-uniform batch offset;
+// no per-lane address arithmetic. The descriptor bounds the wave's range: an offset past it
+// reads zeros instead of memory.
+template <int U>
+__device__ __forceinline__ void load_batch(__amdgpu_buffer_rsrc_t rsrc, int voff, int b,
+                                           u32x4 *buf) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
+        buf[u] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, (b * U + u) * kWave * 16,
+                                                       kNonTemporal);
+}
+
+// Largest element per lane of a batch (only the first `nvalid` vectors are real).
+template <typename T, int U, bool PARTIAL>
+__device__ __forceinline__ void unpack_batch(const u32x4 *buf, int nvalid, int lane, float *x,
+                                             float &bmax) {
+    constexpr int EV = Elem<T>::kPerVec;
 #pragma unroll
-        for (int e = 0; e < EV; ++e) {
-            id[u * EV + e] = id0 + u * kWave * EV + e;
-            valid[u * EV + e] = true;
+    for (int u = 0; u < U; ++u) {
+        Elem<T>::unpack(buf[u], x + u * EV);
+        if (PARTIAL && u * kWave + lane >= nvalid) {
+#pragma unroll
+            for (int e = 0; e < EV; ++e) x[u * EV + e] = -INFINITY;
         }
-    offer<NB>(w, x, id, valid, bmax, lane);
-}
-
-// Elements [e0, e1) of the flat tensor, one per lane per step (ragged row ends).
-template <typename T>
-__device__ __forceinline__ void scalar_range(const T *logits, int64_t e0, int64_t e1, int64_t row_start,
-                             WaveTopk &w, float &ref, float &sum, int lane) {
-    for (int64_t e = e0; e < e1; e += kWave) {
-        const int64_t ei = e + lane;
-        bool valid[1] = {ei < e1};
-        float x[1] = {valid[0] ? Elem<T>::load(logits, ei) : -INFINITY};
-        int32_t id[1] = {(int32_t)(ei - row_start)};
-        lse_update_masked<1>(ref, sum, x, valid, x[0]);
-        offer<1>(w, x, id, valid, x[0], lane);
     }
+    bmax = x[0];
+#pragma unroll
+    for (int j = 1; j < U * EV; ++j) bmax = fmaxf(bmax, x[j]);
 }
 
-template <typename T, int WAVES, int U>
-__global__ __launch_bounds__(WAVES * kWave) void topk_lse_kernel(
+// One batch of the wave's range: vectors vbase + lane + u * 64. PARTIAL: only the first
+// `nvalid` vectors are in range; the others (read as zeros) are replaced by -inf, which adds
+// nothing to the sum and is never a candidate.
+template <typename T, int U, bool PARTIAL>
+__device__ __forceinline__ void batch(const u32x4 *buf, int64_t vbase, int64_t g0, int nvalid,
+                                      WaveTopk &w, float &ref, float &sum, int lane,
+                                      u32x4 *xbuf) {
+    constexpr int EV = Elem<T>::kPerVec;
+    constexpr int NB = U * EV;
+    pull_tau(w);
+    float x[NB], bmax;
+    unpack_batch<T, U, PARTIAL>(buf, nvalid, lane, x, bmax);
+    if (!PARTIAL || bmax != -INFINITY) lse_update<NB>(ref, sum, x, bmax);
+    offer_lanes<T, U, (NB < kWave ? NB : kWave)>(w, buf, bmax, bmax != -INFINITY, nvalid,
+                                                  (int32_t)(vbase * EV - g0), EV, lane, xbuf);
+}
+
+// Threshold seed: the k-th largest lane maximum of the first batch (k real elements reach it;
+// -inf when fewer than k lanes hold data, which admits everything).
+template <typename T, int U, bool PARTIAL>
+__device__ __forceinline__ void seed(const u32x4 *buf, int nvalid, WaveTopk &w, int lane) {
+    float x[U * Elem<T>::kPerVec], bmax;
+    unpack_batch<T, U, PARTIAL>(buf, nvalid, lane, x, bmax);
+    const uint64_t lk = wave_sort_desc((uint64_t)value_key(bmax) << 32, lane);
+    raise_tau(w, lane_value(lk, w.k - 1), lane);
+}
+
+// The ragged ends of a row (its elements outside whole 16-byte vectors) hold fewer than 2 * EV
+// elements: one per lane. They are loaded before the stream starts and offered after it.
+template <typename T>
+__device__ __forceinline__ float ragged_load(const T *logits, int64_t e0, int64_t e1, int lane) {
+    const int64_t e = e0 + lane;
+    return e < e1 ? Elem<T>::load(logits, e) : -INFINITY;
+}
+
+template <typename T>
+__device__ __forceinline__ void ragged_offer(float x, int64_t e0, int64_t e1, int64_t g0,
+                                             WaveTopk &w, float &ref, float &sum, int lane,
+                                             u32x4 *xbuf) {
+    const bool ok = e0 + lane < e1;
+    lse_update_one(ref, sum, x, ok);
+    const u32x4 raw = Elem<T>::single(x);
+    offer_lanes<T, 1, 1>(w, &raw, x, ok, kWave, (int32_t)(e0 - g0), 1, lane, xbuf);
+}
+
+// Grid: R * S workgroups of W = blockDim.x / 64 waves; workgroup (row, slice) covers part
+// slice of the row, wave w sub-part w of it.
+template <typename T, int U, int NBUF>
+__global__ __launch_bounds__(kWave * kMaxWaves) __attribute__((amdgpu_waves_per_eu(4))) void topk_lse_kernel(
     const T *__restrict__ logits, int V, int k, int S, int32_t *__restrict__ cand_ids,
     float *__restrict__ unary, float *__restrict__ lse_out, uint64_t *__restrict__ part_keys,
     float2 *__restrict__ part_lse) {
     constexpr int EV = Elem<T>::kPerVec;
-    constexpr int NB = U * EV;  // elements per lane per batch
-    __shared__ uint64_t stage_all[WAVES][kStageCap];
-    __shared__ uint64_t lists[WAVES][kWave];
-    __shared__ float2 wave_lse[WAVES];
+    constexpr int step = U * kWave;  // vectors per batch
+    extern __shared__ __attribute__((aligned(16))) u32x4 xbuf_all[];  // [W][64 * U]
+    __shared__ uint64_t shared_tau;
+    __shared__ float2 wave_lse[kMaxWaves];
 
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int W = blockDim.x / kWave;
     const int64_t row = blockIdx.x / S;
     const int slice = blockIdx.x % S;
+    u32x4 *xbuf = xbuf_all + wave * (kWave * U);
 
-    // Full 16-byte vectors inside this row: [va, vb); ragged ends are handled element-wise.
+    if (threadIdx.x == 0) shared_tau = 0ull;
+    __syncthreads();
+
+    // Whole 16-byte vectors inside this row: [va, vb), split into S * W parts; this wave takes
+    // part slice * W + wave: [c0, c1).
     const int64_t g0 = row * (int64_t)V, g1 = g0 + V;
     int64_t va = (g0 + EV - 1) / EV, vb = g1 / EV;
     if (va > vb) va = vb = 0;
     const int64_t nvec = vb - va;
-    const int chunks = S * WAVES, chunk = slice * WAVES + wave;
-    const int64_t c0 = va + nvec * chunk / chunks, c1 = va + nvec * (chunk + 1) / chunks;
+    const int parts = S * W, part = slice * W + wave;
+    const int64_t c0 = va + nvec * part / parts, c1 = va + nvec * (part + 1) / parts;
+    const int64_t nv = c1 - c0;
+    const int nfull = (int)(nv / step);
+    const int tail = (int)(nv - (int64_t)nfull * step);  // vectors of the partial last batch
 
     WaveTopk w;
     w.top = 0ull;
     w.tau_key = 0ull;
     w.tau_v = -INFINITY;
-    w.cnt = 0;
-    w.stage = stage_all[wave];
     w.k = k;
+    w.shared_tau = &shared_tau;
     float ref = -INFINITY, sum = 0.0f;
 
-    // Full batches (U vectors per lane), double-buffered: the next batch is in flight while the
-    // current one is processed. The first batch also seeds the threshold.
-    const int64_t step = (int64_t)U * kWave;
-    const int64_t nfull = (c1 - c0) / step;
-    int64_t vbase = c0 + nfull * step;
-    if (nfull > 0) {
-        u32x4 bufA[U], bufB[U];
-        load_batch<T, U>(logits, c0, lane, bufA);
-        if (nfull > 1) load_batch<T, U>(logits, c0 + step, lane, bufB);
-        full_batch<T, U, true>(bufA, c0, g0, k, w, ref, sum, lane);
-        for (int64_t b = 1; b < nfull; b += 2) {
-            if (b + 1 < nfull) load_batch<T, U>(logits, c0 + (b + 1) * step, lane, bufA);
-            full_batch<T, U, false>(bufB, c0 + b * step, g0, k, w, ref, sum, lane);
-            if (b + 1 >= nfull) break;
-            if (b + 2 < nfull) load_batch<T, U>(logits, c0 + (b + 2) * step, lane, bufB);
-            full_batch<T, U, false>(bufA, c0 + (b + 1) * step, g0, k, w, ref, sum, lane);
-        }
-    }
-    // Remaining vectors: one per lane per step.
-    for (; vbase < c1; vbase += kWave) {
-        const int64_t v = vbase + lane;
-        const bool ok = v < c1;
-        u32x4 raw = ok ? load_vec(logits, v) : u32x4{0u, 0u, 0u, 0u};
-        float x[EV];
-        Elem<T>::unpack(raw, x);
-        int32_t id[EV];
-        bool valid[EV];
-        float bmax = -INFINITY;
+    // Ragged row ends (the first part takes the head, the last part the tail), loaded up front.
+    const int64_t h0 = g0, h1 = nvec > 0 ? va * EV : g1, t0 = vb * EV, t1 = g1;
+    const bool do_head = part == 0 && h1 > h0;
+    const bool do_tail = part == parts - 1 && nvec > 0 && t1 > t0;
+    const float xh = do_head ? ragged_load<T>(logits, h0, h1, lane) : -INFINITY;
+    const float xt = do_tail ? ragged_load<T>(logits, t0, t1, lane) : -INFINITY;
+
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u32x4 *>(reinterpret_cast<const u32x4 *>(logits) + c0), 0, (int)(nv * 16),
+        kBufferWord3);
+    const int voff = lane * 16;
+
+    // Batches (the last one partial when tail > 0) go through a ring of NBUF buffers, issued
+    // NBUF - 1 batches ahead of the one processed.
+    const int nall = nfull + (tail > 0 ? 1 : 0);
+    u32x4 ring[NBUF][U];
 #pragma unroll
-        for (int e = 0; e < EV; ++e) {
-            valid[e] = ok;
-            id[e] = (int32_t)(v * EV + e - g0);
-            if (!ok) x[e] = -INFINITY;
-            bmax = fmaxf(bmax, x[e]);
+    for (int i = 0; i < NBUF - 1; ++i)
+        if (i < nall) load_batch<U>(rsrc, voff, i, ring[i]);
+
+    if (nfull > 0)
+        seed<T, U, false>(ring[0], step, w, lane);
+    else if (tail > 0)
+        seed<T, U, true>(ring[0], tail, w, lane);
+
+    for (int b0 = 0; b0 < nfull; b0 += NBUF) {
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j) {
+            const int b = b0 + j;
+            if (b >= nfull) break;
+            if (b + NBUF - 1 < nall)
+                load_batch<U>(rsrc, voff, b + NBUF - 1, ring[(j + NBUF - 1) % NBUF]);
+            batch<T, U, false>(ring[j], c0 + (int64_t)b * step, g0, step, w, ref, sum, lane, xbuf);
         }
-        lse_update_masked<EV>(ref, sum, x, valid, bmax);
-        offer<EV>(w, x, id, valid, bmax, lane);
     }
-    // Ragged ends of the row (fewer than EV elements each, or the whole of a very short row).
-    if (chunk == 0) scalar_range<T>(logits, g0, nvec > 0 ? va * EV : g1, g0, w, ref, sum, lane);
-    if (chunk == chunks - 1 && nvec > 0) scalar_range<T>(logits, vb * EV, g1, g0, w, ref, sum, lane);
-    if (w.cnt > 0) wave_flush(w, lane);
+    if (tail > 0) {
+        // the partial batch sits in ring slot nfull % NBUF (static register indexing)
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j)
+            if (j == nfull % NBUF)
+                batch<T, U, true>(ring[j], c0 + (int64_t)nfull * step, g0, tail, w, ref, sum,
+                                  lane, xbuf);
+    }
+    if (do_head) ragged_offer<T>(xh, h0, h1, g0, w, ref, sum, lane, xbuf);
+    if (do_tail) ragged_offer<T>(xt, t0, t1, g0, w, ref, sum, lane, xbuf);
 
     // (ref, sum) across the wave, fixed butterfly order.
 #pragma unroll
@@ -242,19 +331,22 @@ __global__ __launch_bounds__(WAVES * kWave) void topk_lse_kernel(
         const float osum = __shfl_xor(sum, off, kWave);
         lse_combine(ref, sum, oref, osum);
     }
-    lists[wave][lane] = w.top;
+
+    // Merge the waves' lists and pairs in wave order (wave 0 merges; lists staged in xbuf).
+    uint64_t *lists = reinterpret_cast<uint64_t *>(xbuf_all);  // [W][64]
+    __syncthreads();  // every wave is done with its xbuf
+    lists[wave * kWave + lane] = w.top;
     if (lane == 0) wave_lse[wave] = make_float2(ref, sum);
     __syncthreads();
     if (wave != 0) return;
-
-    uint64_t acc = lists[0][lane];
-    float2 ls = wave_lse[0];
-    for (int q = 1; q < WAVES; ++q) {
-        acc = wave_merge_desc(acc, lists[q][lane], lane);
-        lse_combine(ls.x, ls.y, wave_lse[q].x, wave_lse[q].y);
+    uint64_t acc = w.top;
+    for (int v = 1; v < W; ++v) {
+        acc = wave_merge_desc(acc, lists[v * kWave + lane], lane);
+        const float2 o = wave_lse[v];
+        lse_combine(ref, sum, o.x, o.y);
     }
     if (S == 1) {
-        const double lse = lse_value(ls.x, ls.y);
+        const double lse = lse_value(ref, sum);
         if (lane < k) {
             cand_ids[row * k + lane] = key_id(acc);
             unary[row * k + lane] = (float)((double)key_logit(acc) - lse);
@@ -262,7 +354,7 @@ __global__ __launch_bounds__(WAVES * kWave) void topk_lse_kernel(
         if (lane == 0 && lse_out) lse_out[row] = (float)lse;
     } else {
         part_keys[(row * S + slice) * kWave + lane] = acc;
-        if (lane == 0) part_lse[row * S + slice] = ls;
+        if (lane == 0) part_lse[row * S + slice] = make_float2(ref, sum);
     }
 }
 
@@ -287,12 +379,13 @@ __global__ __launch_bounds__(kWave) void topk_merge_kernel(
     if (lane == 0 && lse_out) lse_out[row] = (float)lse;
 }
 
-template <typename T, int WAVES, int U>
+template <typename T>
 hipError_t launch_k1(const TopkPlan &plan, const void *logits, int R, int V, int k,
                      int32_t *cand_ids, float *unary, float *lse, uint64_t *part_keys,
                      float2 *part_lse, hipStream_t stream) {
-    const dim3 grid((unsigned)(R * plan.slices)), block(WAVES * kWave);
-    hipLaunchKernelGGL((topk_lse_kernel<T, WAVES, U>), grid, block, 0, stream,
+    const dim3 grid((unsigned)(R * plan.slices)), block(kWave * plan.waves);
+    const size_t lds = (size_t)plan.waves * kWave * kU * sizeof(u32x4);
+    hipLaunchKernelGGL((topk_lse_kernel<T, kU, kRing>), grid, block, lds, stream,
                        static_cast<const T *>(logits), V, k, plan.slices, cand_ids, unary, lse,
                        part_keys, part_lse);
     hipError_t e = hipGetLastError();
@@ -305,16 +398,21 @@ hipError_t launch_k1(const TopkPlan &plan, const void *logits, int R, int V, int
 }  // namespace
 
 TopkPlan plan_topk(int R, int V, int elem_bytes) {
+    // About 4096 waves (16 per CU, 4 per SIMD), each streaming at least 2 batches: as many waves
+    // per row as that allows (up to kMaxWaves in one workgroup), then slices if rows are still too few.
+    const int64_t target_waves = 4096;
+    const int64_t batch_elems = (int64_t)kWave * kU * (16 / elem_bytes);
+    int64_t max_parts = (int64_t)V / (batch_elems * 2);
+    if (max_parts < 1) max_parts = 1;
+    int64_t want = (target_waves + R - 1) / R;
+    if (want > max_parts) want = max_parts;
+    if (want < 1) want = 1;
     TopkPlan p;
-    p.waves = 4;
-    // Enough workgroups to cover the chip, but at least ~4 full batches per wave.
-    const int64_t target_wgs = 1024;
-    const int64_t batch_elems = (int64_t)kWave * 4 * (16 / elem_bytes);
-    const int64_t max_slices = (int64_t)V / (batch_elems * 4 * p.waves);
-    int64_t s = (target_wgs + R - 1) / R;
-    if (s > max_slices) s = max_slices;
-    if (s < 1) s = 1;
-    p.slices = (int)s;
+    p.waves = 1;
+    while (p.waves * 2 <= want && p.waves * 2 <= kMaxWaves) p.waves *= 2;
+    p.slices = (int)((want + p.waves - 1) / p.waves);
+    if ((int64_t)p.slices * p.waves > max_parts) p.slices = (int)(max_parts / p.waves);
+    if (p.slices < 1) p.slices = 1;
     return p;
 }
 
@@ -330,10 +428,10 @@ hipError_t launch_topk_lse(const void *logits, int logits_dtype, int R, int V, i
     uint64_t *part_keys = static_cast<uint64_t *>(workspace);
     float2 *part_lse = reinterpret_cast<float2 *>(part_keys + (size_t)R * plan.slices * kWave);
     if (logits_dtype == 0)
-        return launch_k1<float, 4, 4>(plan, logits, R, V, k, cand_ids, unary, lse, part_keys,
-                                      part_lse, stream);
-    return launch_k1<uint16_t, 4, 4>(plan, logits, R, V, k, cand_ids, unary, lse, part_keys,
-                                     part_lse, stream);
+        return launch_k1<float>(plan, logits, R, V, k, cand_ids, unary, lse, part_keys, part_lse,
+                                stream);
+    return launch_k1<uint16_t>(plan, logits, R, V, k, cand_ids, unary, lse, part_keys, part_lse,
+                               stream);
 }
 
 }  // namespace dflash2

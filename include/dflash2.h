@@ -46,6 +46,7 @@ extern "C" {
 #define DFLASH2_ABI_VERSION 1
 #define DFLASH2_MAX_K 64  /* largest top-k */
 #define DFLASH2_MAX_R 256 /* largest codebook rank r */
+#define DFLASH2_MAX_V (1 << 28) /* largest vocabulary (a row's bytes stay within 32-bit offsets) */
 
 typedef enum dflash2_dtype {
     DFLASH2_F32 = 0,  /* IEEE binary32 */
@@ -77,7 +78,8 @@ const char *dflash2_status_string(int status);
  *   pred_cb     [V, r]     cb_dtype, device. Predecessor codebook A.
  *   succ_cb     [V, r]     cb_dtype, device. Successor codebook B.
  *   anchor_ids  [B]        int32, device. Last verified token of each sequence.
- *   B, L, V, H, r, k       B, L, V, H >= 1; 1 <= r <= DFLASH2_MAX_R; 1 <= k <= min(V, DFLASH2_MAX_K).
+ *   B, L, V, H, r, k       B, L, H >= 1; 1 <= V <= DFLASH2_MAX_V; 1 <= r <= DFLASH2_MAX_R;
+ *                          1 <= k <= min(V, DFLASH2_MAX_K).
  * Outputs (device, written in full):
  *   cand_ids    [B, L, k]     int32. The first k tokens of the candidate order.
  *   unary       [B, L, k]     float. logit - logsumexp(row), in candidate order.
