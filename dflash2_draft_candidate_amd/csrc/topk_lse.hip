@@ -24,8 +24,8 @@
 //     lane's elements back transposed (lane j <- element j). Each candidate is inserted straight
 //     into the sorted list (rank by ballot + popcount, a one-lane DPP shift), and the wave's
 //     k-th key is read back with readlane.
-//   * The threshold starts at the k-th largest of the 64 lane maxima of each wave's first batch
-//     (k real elements reach it).
+//   * The threshold starts at the k-th largest of the lane maxima of all the workgroup's waves
+//     over their first NBUF - 1 batches (k real elements reach it).
 //   * The waves' lists and (ref, sum) pairs are merged in wave order at the end.
 // All orders are fixed and the merged top-k of distinct keys is unique, so results are
 // deterministic.
@@ -207,14 +207,22 @@ __device__ __forceinline__ void batch(const u32x4 *buf, int64_t vbase, int64_t g
                                                   (int32_t)(vbase * EV - g0), EV, lane, xbuf);
 }
 
-// Threshold seed: the k-th largest lane maximum of the first batch (k real elements reach it;
-// -inf when fewer than k lanes hold data, which admits everything).
-template <typename T, int U, bool PARTIAL>
-__device__ __forceinline__ void seed(const u32x4 *buf, int nvalid, WaveTopk &w, int lane) {
-    float x[U * Elem<T>::kPerVec], bmax;
-    unpack_batch<T, U, PARTIAL>(buf, nvalid, lane, x, bmax);
-    const uint64_t lk = wave_sort_desc((uint64_t)value_key(bmax) << 32, lane);
-    raise_tau(w, lane_value(lk, w.k - 1), lane);
+// Largest element of each lane over the batches already in the ring (the first NBUF - 1; the
+// batch with index nfull is the partial one, with `tail` vectors). -inf for a lane with no data.
+template <typename T, int U, int NBUF>
+__device__ __forceinline__ float seed_lane_max(const u32x4 (*ring)[U], int nfull, int tail,
+                                               int lane) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) {
+        float x[U * Elem<T>::kPerVec], bmax = -INFINITY;
+        if (i < nfull)
+            unpack_batch<T, U, false>(ring[i], kWave * U, lane, x, bmax);
+        else if (i == nfull && tail > 0)
+            unpack_batch<T, U, true>(ring[i], tail, lane, x, bmax);
+        m = fmaxf(m, bmax);
+    }
+    return m;
 }
 
 // The ragged ends of a row (its elements outside whole 16-byte vectors) hold fewer than 2 * EV
@@ -247,6 +255,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) __attribute__((amdgpu_waves_per_
     extern __shared__ __attribute__((aligned(16))) u32x4 xbuf_all[];  // [W][64 * U]
     __shared__ uint64_t shared_tau;
     __shared__ float2 wave_lse[kMaxWaves];
+    __shared__ uint64_t seed_keys[kMaxWaves * kWave];
 
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -255,8 +264,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) __attribute__((amdgpu_waves_per_
     const int slice = blockIdx.x % S;
     u32x4 *xbuf = xbuf_all + wave * (kWave * U);
 
-    if (threadIdx.x == 0) shared_tau = 0ull;
-    __syncthreads();
+    if (threadIdx.x == 0) shared_tau = 0ull;  // published to the other waves by the seed barrier
 
     // Whole 16-byte vectors inside this row: [va, vb), split into S * W parts; this wave takes
     // part slice * W + wave: [c0, c1).
@@ -298,10 +306,17 @@ __global__ __launch_bounds__(kWave * kMaxWaves) __attribute__((amdgpu_waves_per_
     for (int i = 0; i < NBUF - 1; ++i)
         if (i < nall) load_batch<U>(rsrc, voff, i, ring[i]);
 
-    if (nfull > 0)
-        seed<T, U, false>(ring[0], step, w, lane);
-    else if (tail > 0)
-        seed<T, U, true>(ring[0], tail, w, lane);
+    // Threshold seed: the k-th largest of the lane maxima of all waves over the preloaded
+    // batches (k real elements reach it; -inf, which admits everything, when fewer than k lanes
+    // hold data). The waves' ranges are disjoint, so the maxima are distinct elements.
+    seed_keys[wave * kWave + lane] = wave_sort_desc(
+        (uint64_t)value_key(seed_lane_max<T, U, NBUF>(ring, nfull, tail, lane)) << 32, lane);
+    __syncthreads();
+    {
+        uint64_t u = seed_keys[lane];
+        for (int v = 1; v < W; ++v) u = wave_merge_desc(u, seed_keys[v * kWave + lane], lane);
+        raise_tau(w, lane_value(u, k - 1), lane);
+    }
 
     for (int b0 = 0; b0 < nfull; b0 += NBUF) {
 #pragma unroll
