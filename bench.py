@@ -31,6 +31,9 @@ PEAK_HBM_GBS = 8000.0
 POOL_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "topk_lse_traffic.json")
 K1_SOURCE = os.path.join(ROOT, "dflash2_draft_candidate_amd", "csrc", "topk_lse.hip")
+K1_KERNEL = "topk_lse_kernel"
+COPY_KERNEL = "copyBuffer"  # the HIP runtime's device-to-device copy kernel
+COPY_REPS = 5
 
 
 def log(*a):
@@ -138,7 +141,7 @@ def measure(name: str, device: str, steps: int, warmup: int) -> dict:
     return res
 
 
-def cpu_baseline(name: str, min_seconds: float = 10.0, max_passes: int = 8) -> dict:
+def cpu_baseline(name: str, min_seconds: float = 12.0, max_passes: int = 64) -> dict:
     """The oracle (fp64 C, one thread) on the host over whole passes of the workload."""
     import oracle
     import synth
@@ -169,6 +172,92 @@ def committed_traffic() -> dict | None:
     return t
 
 
+def _kernel_name(n: str) -> str:
+    n = n.replace("void ", "").replace("dflash2::(anonymous namespace)::", "")
+    return n.split("(")[0]
+
+
+def _counter_rows(path: str, counter: str):
+    """(kernel name, value) of every dispatch in a rocprofv3 counter_collection.csv, in dispatch
+    order."""
+    import csv
+    rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows]
+
+
+def summarize(a: list[str]):
+    """Write a profiles/ summary from rocprofv3 output (runs on the host, no GPU)."""
+    import csv
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    if a[0] == "trace":
+        stats, out_md, cmd = a[1], a[2], a[3]
+        lines = [f"# Kernel trace: {os.path.basename(out_md)[:-3]}", "",
+                 "Command (from the repository root on a one-GPU MI355X box):", "",
+                 f"    {cmd}", "",
+                 "| kernel | calls | avg us | min us | max us | share of GPU time |",
+                 "|---|---|---|---|---|---|"]
+        for r in csv.DictReader(open(stats)):
+            lines.append(f"| `{_kernel_name(r['Name'])}` | {r['Calls']} | "
+                         f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                         f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+        open(out_md, "w").write("\n".join(lines) + "\n")
+        print(out_md)
+        return
+    if a[0] == "traffic":
+        import synth
+        fetch_csv, write_csv, workload, cmd = a[1], a[2], a[3], a[4]
+        reads = {}
+        for which, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"),
+                                     ("write", write_csv, "WRITE_SIZE")):
+            rows = _counter_rows(path, counter)
+            k1 = [v for n, v in rows if K1_KERNEL in n]
+            # the calibration copies are the last COPY_REPS copies (earlier ones build the pool)
+            cp = [v for n, v in rows if COPY_KERNEL in n][-COPY_REPS:]
+            if not k1 or not cp:
+                raise SystemExit(f"{path}: no {K1_KERNEL} or {COPY_KERNEL} dispatches")
+            reads[which] = (sum(k1) / len(k1), sum(cp) / len(cp), len(k1), len(cp))
+        copy_bytes = int(cmd.split("--copy-mib")[1].split()[0]) << 20
+        f_k1, f_cp, n1, n2 = reads["fetch"]
+        w_k1, w_cp, _, _ = reads["write"]
+        f_factor = f_cp * 1024 / copy_bytes  # counter bytes per byte really read
+        w_factor = w_cp * 1024 / copy_bytes
+        fetch_b = f_k1 * 1024 / f_factor
+        write_b = w_k1 * 1024 / w_factor
+        s = synth.spec(workload)
+        t = {"kernel": K1_KERNEL, "workload": workload,
+             "k1_source_sha256_16": source_hash(K1_SOURCE),
+             "bytes_per_launch": int(round(fetch_b + write_b)),
+             "fetch_bytes_per_launch": int(round(fetch_b)),
+             "write_bytes_per_launch": int(round(write_b)),
+             "algorithmic_bytes_per_launch": k1_bytes(s),
+             "raw_fetch_kib_per_launch": round(f_k1, 1), "raw_write_kib_per_launch": round(w_k1, 1),
+             "copy_bytes": copy_bytes, "copy_fetch_kib": round(f_cp, 1),
+             "copy_write_kib": round(w_cp, 1), "fetch_factor": round(f_factor, 4),
+             "write_factor": round(w_factor, 4), "k1_dispatches": n1, "copy_dispatches": n2,
+             "command": cmd}
+        json.dump(t, open(TRAFFIC_FILE, "w"), indent=1)
+        md = os.path.join(ROOT, "profiles", f"topk_lse_{workload}_traffic.md")
+        open(md, "w").write(
+            f"# HBM traffic of {K1_KERNEL} on {workload}\n\n"
+            "Two rocprofv3 counter passes over the same command (FETCH_SIZE, then WRITE_SIZE), "
+            "from the repository root on a one-GPU MI355X box:\n\n"
+            f"    rocprofv3 --pmc FETCH_SIZE ... -- {cmd}\n"
+            f"    rocprofv3 --pmc WRITE_SIZE ... -- {cmd}\n\n"
+            f"Calibration: the runtime's copy kernel moving {copy_bytes} bytes reads "
+            f"{f_cp:.1f} KiB of FETCH_SIZE and {w_cp:.1f} KiB of WRITE_SIZE per dispatch: "
+            f"factors {f_factor:.4f} (fetch) and {w_factor:.4f} (write) counter bytes per byte.\n\n"
+            f"| per K1 launch | bytes |\n|---|---|\n"
+            f"| FETCH_SIZE raw | {f_k1 * 1024:.0f} |\n| WRITE_SIZE raw | {w_k1 * 1024:.0f} |\n"
+            f"| fetch (calibrated) | {fetch_b:.0f} |\n| write (calibrated) | {write_b:.0f} |\n"
+            f"| traffic (calibrated) | {fetch_b + write_b:.0f} |\n"
+            f"| algorithmic | {k1_bytes(s)} |\n"
+            f"| traffic / algorithmic | {(fetch_b + write_b) / k1_bytes(s):.4f} |\n")
+        print(TRAFFIC_FILE, md)
+        return
+    raise SystemExit(f"unknown summary kind {a[0]}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -179,7 +268,16 @@ def main():
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--k1-only", action="store_true",
                     help="only loop K1 launches (for counter collection), no JSON")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="with --k1-only: also run device-to-device copies of this many MiB, the "
+                         "calibration for the HBM byte counters")
+    ap.add_argument("--summarize", nargs="+", metavar="ARG",
+                    help="no GPU: 'trace STATS_CSV OUT_MD CMD' or 'traffic FETCH_CSV WRITE_CSV "
+                         "WORKLOAD CMD' writes a profiles/ summary from rocprofv3 output")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (each sequence is "
               "independent; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
@@ -204,6 +302,14 @@ def main():
         ms = time_loop(lambda i: w.k1_step(i, ids, unary, lse, ws), args.steps, args.warmup)
         log(f"[bench] k1-only {args.workload}: {ms * 1e3:.2f} us/launch, "
             f"{k1_bytes(s) / (ms * 1e-3) / 1e9:.1f} GB/s")
+        if args.copy_mib > 0:
+            n = args.copy_mib << 20
+            src = torch.empty(n, dtype=torch.uint8, device=device).fill_(1)
+            dst = torch.empty_like(src)
+            for _ in range(COPY_REPS):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            log(f"[bench] {COPY_REPS} device copies of {args.copy_mib} MiB done")
         return
 
     main_res = measure(args.workload, device, args.steps, args.warmup)
