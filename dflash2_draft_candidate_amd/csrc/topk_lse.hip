@@ -63,6 +63,9 @@ struct WaveTopk {
     float tau_v;       // logit of the threshold, for the cheap first test
     int k;
     uint64_t *shared_tau;  // the workgroup threshold in LDS
+    uint64_t *pub;         // per wave of the workgroup: its list's n-th key (n = ceil(k / W))
+    uint64_t pub_mine;     // what this wave last published
+    int n, W, wave;
 };
 
 __device__ __forceinline__ void set_tau(WaveTopk &w, uint64_t key) {
@@ -89,6 +92,28 @@ __device__ __forceinline__ void pull_tau(WaveTopk &w) {
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(s >> 32));
     const uint64_t su = ((uint64_t)hi << 32) | lo;
     if (su > w.tau_key) set_tau(w, su);
+}
+
+// After a batch that changed the list: publish its n-th key and raise the workgroup threshold to
+// the smallest n-th key over the W waves. Every wave has n distinct elements at or above its
+// published key (a list position only ever grows), and W * n >= k, so k real elements reach
+// that minimum: a valid threshold, usually well above the largest single-wave k-th key.
+__device__ __forceinline__ void publish_and_refresh(WaveTopk &w, int lane) {
+    const uint64_t mine = lane_value(w.top, w.n - 1);
+    if (mine <= w.pub_mine) return;
+    w.pub_mine = mine;
+    if (lane == 0)
+        __hip_atomic_store(&w.pub[w.wave], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint64_t p = lane < w.W ? __hip_atomic_load(&w.pub[lane], __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_WORKGROUP)
+                                  : ~0ull;
+    uint64_t lo = lane == w.wave ? mine : p;  // this wave's own value, not a stale read
+#pragma unroll
+    for (int off = 1; off < kMaxWaves; off <<= 1) {
+        const uint64_t o = __shfl_xor(lo, off, kWave);
+        lo = o < lo ? o : lo;
+    }
+    raise_tau(w, lane_value(lo, 0), lane);
 }
 
 // Insert key c (wave-uniform, above the threshold) into the sorted list: its rank is the number
@@ -139,6 +164,7 @@ __device__ __forceinline__ void offer_lanes(WaveTopk &w, const u32x4 *buf, float
             }
         }
     }
+    publish_and_refresh(w, lane);
 }
 
 // One lane's online logsumexp update with NB elements (-inf elements add nothing).
@@ -256,6 +282,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) __attribute__((amdgpu_waves_per_
     __shared__ uint64_t shared_tau;
     __shared__ float2 wave_lse[kMaxWaves];
     __shared__ uint64_t seed_keys[kMaxWaves * kWave];
+    __shared__ uint64_t pub[kMaxWaves];
 
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -265,6 +292,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) __attribute__((amdgpu_waves_per_
     u32x4 *xbuf = xbuf_all + wave * (kWave * U);
 
     if (threadIdx.x == 0) shared_tau = 0ull;  // published to the other waves by the seed barrier
+    if (threadIdx.x < kMaxWaves) pub[threadIdx.x] = 0ull;
 
     // Whole 16-byte vectors inside this row: [va, vb), split into S * W parts; this wave takes
     // part slice * W + wave: [c0, c1).
@@ -284,6 +312,11 @@ __global__ __launch_bounds__(kWave * kMaxWaves) __attribute__((amdgpu_waves_per_
     w.tau_v = -INFINITY;
     w.k = k;
     w.shared_tau = &shared_tau;
+    w.pub = pub;
+    w.pub_mine = 0ull;
+    w.W = W;
+    w.n = (k + W - 1) / W;
+    w.wave = wave;
     float ref = -INFINITY, sum = 0.0f;
 
     // Ragged row ends (the first part takes the head, the last part the tail), loaded up front.
