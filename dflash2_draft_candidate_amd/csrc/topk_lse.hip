@@ -104,16 +104,17 @@ __device__ __forceinline__ void publish_and_refresh(WaveTopk &w, int lane) {
     w.pub_mine = mine;
     if (lane == 0)
         __hip_atomic_store(&w.pub[w.wave], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    // lane v reads wave v's key; the minimum is taken over wave-uniform values (scalar unit)
     const uint64_t p = lane < w.W ? __hip_atomic_load(&w.pub[lane], __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_WORKGROUP)
                                   : ~0ull;
-    uint64_t lo = lane == w.wave ? mine : p;  // this wave's own value, not a stale read
-#pragma unroll
-    for (int off = 1; off < kMaxWaves; off <<= 1) {
-        const uint64_t o = __shfl_xor(lo, off, kWave);
+    uint64_t lo = mine;  // this wave's own value, not a stale read
+    for (int v = 0; v < w.W; ++v) {
+        if (v == w.wave) continue;
+        const uint64_t o = lane_value(p, v);
         lo = o < lo ? o : lo;
     }
-    raise_tau(w, lane_value(lo, 0), lane);
+    raise_tau(w, lo, lane);
 }
 
 // Insert key c (wave-uniform, above the threshold) into the sorted list: its rank is the number
@@ -145,7 +146,6 @@ __device__ __forceinline__ void offer_lanes(WaveTopk &w, const u32x4 *buf, float
         for (int u = 0; u < U; ++u) xbuf[lane * U + u] = buf[u];
     }
     const int j = lane;  // this lane reads element j of each publishing lane
-    const int32_t id_j = (j / EV) * kWave * EV + (j % EV);
     const int vec_j = (j / EV) * kWave;
     while (hits != 0ull) {
         const int L = __builtin_ctzll(hits);
@@ -153,15 +153,15 @@ __device__ __forceinline__ void offer_lanes(WaveTopk &w, const u32x4 *buf, float
         float x = -INFINITY;
         if (j < NSLOT) x = Elem<T>::lds_element(xbuf, L * U * EV + j);
         const bool maybe = j < NSLOT && vec_j + L < nvalid && x >= w.tau_v && x != -INFINITY;
-        if (__ballot(maybe) != 0ull) {
-            const uint64_t key = cand_key(x, id_base + L * lane_stride + id_j);
-            uint64_t m = __ballot(maybe && key > w.tau_key);
-            while (m != 0ull) {
-                const int src = __builtin_ctzll(m);
-                m &= m - 1ull;
-                const uint64_t c = lane_value(key, src);
-                if (c > w.tau_key) wave_insert(w, c, lane);
-            }
+        uint64_t m = __ballot(maybe);
+        while (m != 0ull) {
+            // each candidate's key is built from wave-uniform values (scalar unit)
+            const int src = __builtin_ctzll(m);
+            m &= m - 1ull;
+            const float xs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), src));
+            const int32_t id = id_base + L * lane_stride + (src / EV) * kWave * EV + (src % EV);
+            const uint64_t c = cand_key(xs, id);
+            if (c > w.tau_key) wave_insert(w, c, lane);
         }
     }
     publish_and_refresh(w, lane);
