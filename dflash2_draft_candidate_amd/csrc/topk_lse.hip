@@ -281,7 +281,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) __attribute__((amdgpu_waves_per_
     extern __shared__ __attribute__((aligned(16))) u32x4 xbuf_all[];  // [W][64 * U]
     __shared__ uint64_t shared_tau;
     __shared__ float2 wave_lse[kMaxWaves];
-    __shared__ uint64_t seed_keys[kMaxWaves * kWave];
+    __shared__ uint32_t seed_vals[kMaxWaves * kWave];
     __shared__ uint64_t pub[kMaxWaves];
 
     const int lane = threadIdx.x % kWave;
@@ -332,23 +332,34 @@ __global__ __launch_bounds__(kWave * kMaxWaves) __attribute__((amdgpu_waves_per_
     const int voff = lane * 16;
 
     // Batches (the last one partial when tail > 0) go through a ring of NBUF buffers, issued
-    // NBUF - 1 batches ahead of the one processed.
+    // NBUF - 1 batches ahead of the one processed; all NBUF are in flight during the seed.
     const int nall = nfull + (tail > 0 ? 1 : 0);
     u32x4 ring[NBUF][U];
 #pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i)
+    for (int i = 0; i < NBUF; ++i)
         if (i < nall) load_batch<U>(rsrc, voff, i, ring[i]);
 
-    // Threshold seed: the k-th largest of the lane maxima of all waves over the preloaded
+    // Threshold seed: the k-th largest of the lane maxima of all waves over their first NBUF - 1
     // batches (k real elements reach it; -inf, which admits everything, when fewer than k lanes
-    // hold data). The waves' ranges are disjoint, so the maxima are distinct elements.
-    seed_keys[wave * kWave + lane] = wave_sort_desc(
-        (uint64_t)value_key(seed_lane_max<T, U, NBUF>(ring, nfull, tail, lane)) << 32, lane);
+    // hold data). The waves' ranges are disjoint, so the maxima are distinct elements. Found as
+    // the largest order-preserving value key t with at least k maxima at or above it, one bit at
+    // a time from the top with ballot counts: no cross-lane data movement.
+    seed_vals[wave * kWave + lane] = value_key(seed_lane_max<T, U, NBUF>(ring, nfull, tail, lane));
     __syncthreads();
     {
-        uint64_t u = seed_keys[lane];
-        for (int v = 1; v < W; ++v) u = wave_merge_desc(u, seed_keys[v * kWave + lane], lane);
-        raise_tau(w, lane_value(u, k - 1), lane);
+        uint32_t v[kMaxWaves];
+#pragma unroll
+        for (int i = 0; i < kMaxWaves; ++i) v[i] = i < W ? seed_vals[i * kWave + lane] : 0u;
+        uint32_t t = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t c = t | (1u << bit);
+            int n = 0;
+#pragma unroll
+            for (int i = 0; i < kMaxWaves; ++i)
+                if (i < W) n += __popcll(__ballot(v[i] >= c));
+            if (n >= k) t = c;
+        }
+        raise_tau(w, (uint64_t)t << 32, lane);
     }
 
     for (int b0 = 0; b0 < nfull; b0 += NBUF) {
@@ -356,7 +367,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) __attribute__((amdgpu_waves_per_
         for (int j = 0; j < NBUF; ++j) {
             const int b = b0 + j;
             if (b >= nfull) break;
-            if (b + NBUF - 1 < nall)
+            if (b >= 1 && b + NBUF - 1 < nall)  // batch NBUF - 1 was loaded before the seed
                 load_batch<U>(rsrc, voff, b + NBUF - 1, ring[(j + NBUF - 1) % NBUF]);
             batch<T, U, false>(ring[j], c0 + (int64_t)b * step, g0, step, w, ref, sum, lane, xbuf);
         }
