@@ -9,8 +9,11 @@ namespace dflash2 {
 
 // ---- K1: top-k + logsumexp -----------------------------------------------------------------
 struct TopkPlan {
-    int waves;   // waves per workgroup
-    int slices;  // workgroups per row; > 1 adds a merge kernel and needs workspace
+    int waves;          // waves per (row, slice) unit
+    int slices;         // slices per row; > 1 adds a merge kernel and needs workspace
+    int groups;         // units per workgroup
+    int chunk_batches;  // batches per chunk handed to a wave
+    int chunks;         // chunks per unit (at most)
 };
 TopkPlan plan_topk(int R, int V, int elem_bytes);
 size_t topk_workspace_bytes(const TopkPlan &plan, int R);

@@ -6,38 +6,53 @@
 // (top 16 candidates per position; unary term U_t(b)); "DFlash2 Lands in llama.cpp" (ramgpt.org),
 // section "What llama.cpp Actually Builds for the Selector" (per-position top-k, gathered unary).
 //
-// Design (gfx950, wave64): a workgroup of W waves per (row, slice); each wave streams its own
-// contiguous part of the row. W is chosen so that about 16 waves share a CU (4 per SIMD): the
-// SIMD then overlaps one wave's arithmetic with the other waves' loads. A row has S slices
-// (S = 1 unless rows are too few to fill the chip; the slices are merged by a second kernel in
-// slice order).
-//   * Streaming: lanes read 16-byte vectors (consecutive lanes consecutive vectors) through a
-//     buffer descriptor bounded to the wave's range, U vectors per lane per batch, NBUF - 1
-//     batches issued ahead of the one processed.
-//   * logsumexp: each lane keeps an online (ref, sum) pair in the log2 domain: one v_exp per
-//     element plus one rescale per batch.
-//   * top-k: each wave keeps its 64 best keys sorted across its lanes (lane = rank). An element
-//     is admitted only if it beats the workgroup threshold: the largest k-th key any wave of the
-//     workgroup holds, shared through LDS (each such key has k keys at or above it, so nothing
-//     below it can be in the row's top k). A batch costs one compare per lane when no lane beats
-//     it. Otherwise the lanes that do publish their raw batch to LDS and the wave reads each such
-//     lane's elements back transposed (lane j <- element j). Each candidate is inserted straight
-//     into the sorted list (rank by ballot + popcount, a one-lane DPP shift), and the wave's
-//     k-th key is read back with readlane.
-//   * The threshold starts at the k-th largest of the lane maxima of all the workgroup's waves
-//     over their first NBUF - 1 batches (k real elements reach it).
-//   * The waves' lists and (ref, sum) pairs are merged in wave order at the end.
-// All orders are fixed and the merged top-k of distinct keys is unique, so results are
-// deterministic.
+// Design (gfx950, wave64). A unit is a (row, slice) pair (S slices per row; S = 1 unless rows
+// are too few to fill the chip, and then a second kernel merges the slices in slice order). One
+// workgroup of 16 waves fills a CU and owns G units; W = 16 / G waves stream each unit.
+//   * Balance. The SIMD issues oldest-first, so with a static split the youngest wave on each
+//     SIMD finished far behind the oldest. Here a unit's waves are taken from different age
+//     classes (slots w, w + 4, ... sit on one SIMD with ages 0, 1, ...), so every unit streams at
+//     the same total rate, and they share the unit's chunks (CB batches of 4 vectors per lane)
+//     through an LDS counter, so a favoured wave simply takes more chunks.
+//   * Streaming. Lanes read 16-byte vectors (consecutive lanes, consecutive vectors) through a
+//     buffer descriptor bounded to the unit (an offset past it reads zeros), with a ring of
+//     kRing batches in registers, kRing - 1 issued ahead of the one processed.
+//   * logsumexp with a fixed reference. The unit's reference R (log2 domain) is the largest lane
+//     maximum seen by the seed below. Each lane sums 2^(x log2e - R) over a chunk (one v_exp per
+//     element, no per-batch rescale) and stores the sum to LDS; the sums are added per lane in
+//     chunk order at the end, so the result does not depend on which wave took which chunk. A
+//     chunk whose sum leaves the safe fp32 range (an element far above every seeded maximum)
+//     sends the unit down a slow exact path at the end.
+//   * top-k. A 64-bit key (order-preserving logit map above the inverted id) makes the candidate
+//     order one unsigned compare. Each wave keeps its 64 best keys of the unit sorted across its
+//     lanes. An element is admitted only if it beats the unit's threshold in LDS, which is always
+//     valid (k real elements at or above it): the largest single-wave k-th key, or the smallest
+//     over the W waves of their ceil(k / W)-th keys. A batch costs one compare per lane unless
+//     some lane's maximum reaches it; then each such lane's batch is staged in LDS and read back
+//     transposed (lane j <- element j), and each surviving candidate is inserted by ballot +
+//     popcount rank and a one-lane DPP shift.
+//   * Seed. The threshold starts at the k-th largest of the lane maxima of the unit's waves over
+//     their first batches (k real elements reach it).
+//   * End. The unit's W lists are merged by a tree of bitonic merges (the top k of distinct keys
+//     is unique) and the unit's first wave writes the results. Deterministic throughout.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace dflash2 {
 namespace {
 
-constexpr int kU = 4;     // 16-byte vectors per lane per batch
-constexpr int kRing = 3;  // batches in flight per wave (kRing - 1 ahead of the one processed)
-constexpr int kMaxWaves = 8;              // waves per workgroup (LDS: 4 KB each)
+constexpr int kU = 4;                     // 16-byte vectors per lane per batch
+constexpr int kStep = kU * kWave;         // vectors per batch
+constexpr int kRing = 3;                  // batch buffers per wave (kRing - 1 loads ahead)
+constexpr int kWaves = 16;                // waves per workgroup: one workgroup fills a CU
+constexpr int kThreads = kWaves * kWave;
+constexpr int kMaxUnits = 8;              // units per workgroup (W = kWaves / G >= 2)
+constexpr int kTargetWorkgroups = 256;    // one per CU
+constexpr int kMinBatchesPerWave = 2;     // slices are not cut smaller than this per wave
+constexpr size_t kLdsBudget = 120 * 1024; // dynamic LDS (chunk sums) per workgroup
+constexpr float kSumLimit = 0x1p100f;     // a chunk sum above this leaves the fast path
+constexpr float kTermMargin = 1.f - 0x1p-10f;  // v_exp_f32 is far more accurate than this
+constexpr int kMaxSumHits = 4;            // lanes the sum filter may flag before maxima decide
 constexpr int kBufferWord3 = 0x00020000;  // gfx9-family buffer descriptor word 3 (raw data)
 constexpr int kNonTemporal = 2;           // cache policy: streaming data, read once
 constexpr int kDppWaveShr1 = 0x138;       // DPP control: lane i reads lane i - 1
@@ -49,6 +64,14 @@ __device__ __forceinline__ uint64_t lane_value(uint64_t v, int src) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// A value every lane holds (read back from LDS) as a wave-uniform value. readfirstlane returns
+// int: widen through uint32_t (no sign extension into the high half).
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
 // Lane i receives lane i - 1's value (lane 0 receives 0).
 __device__ __forceinline__ uint64_t shift_up_one(uint64_t v) {
     const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, kDppWaveShr1, 0xF, 0xF, false);
@@ -57,15 +80,29 @@ __device__ __forceinline__ uint64_t shift_up_one(uint64_t v) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// Per-workgroup state in LDS (besides the chunk sums).
+struct K1Shared {
+    uint64_t tau[kMaxUnits];          // admission threshold of each unit
+    uint64_t pub[kWaves];             // per wave: its list's n-th key (n = ceil(k / W))
+    uint64_t lists[kWaves * kWave];   // the waves' lists, for the final merge
+    uint32_t seed_vals[kWaves * kWave];
+    float rag[kMaxUnits * kWave];     // the unit's ragged-end sums per lane
+    u32x4 stage[kWaves][kU];          // per wave: one hit lane's batch, read back transposed
+    uint32_t next_chunk[kMaxUnits];   // next chunk of the unit to hand out
+    uint32_t overflow[kMaxUnits];     // a chunk sum left the safe range
+};
+
 struct WaveTopk {
-    uint64_t top;      // this lane's entry of the wave's sorted list (lane = rank)
-    uint64_t tau_key;  // admission threshold (wave-uniform): a key must exceed it
-    float tau_v;       // logit of the threshold, for the cheap first test
+    uint64_t top;          // this lane's entry of the wave's sorted list (lane = rank)
+    uint64_t tau_key;      // admission threshold (wave-uniform): a key must exceed it
+    float tau_v;           // logit of the threshold, for the cheap first test
     int k;
-    uint64_t *shared_tau;  // the workgroup threshold in LDS
-    uint64_t *pub;         // per wave of the workgroup: its list's n-th key (n = ceil(k / W))
+    uint64_t *shared_tau;  // the unit's threshold in LDS
+    uint64_t *pub;         // the unit's published keys, indexed by wave slot
     uint64_t pub_mine;     // what this wave last published
-    int n, W, wave;
+    int n;                 // ceil(k / W)
+    int slot;              // this wave's slot in the workgroup
+    uint32_t peers;        // bit s: slot s streams the same unit
 };
 
 __device__ __forceinline__ void set_tau(WaveTopk &w, uint64_t key) {
@@ -73,7 +110,7 @@ __device__ __forceinline__ void set_tau(WaveTopk &w, uint64_t key) {
     w.tau_v = key_logit(key);
 }
 
-// The wave's own k-th key rose to `key`: adopt it and publish it to the workgroup.
+// A valid threshold `key` was found: adopt it and publish it to the unit.
 __device__ __forceinline__ void raise_tau(WaveTopk &w, uint64_t key, int lane) {
     if (key > w.tau_key) {
         set_tau(w, key);
@@ -83,19 +120,15 @@ __device__ __forceinline__ void raise_tau(WaveTopk &w, uint64_t key, int lane) {
     }
 }
 
-// Adopt the workgroup threshold if another wave has raised it past ours.
+// The unit's current threshold (other waves may have raised it).
 __device__ __forceinline__ void pull_tau(WaveTopk &w) {
-    const uint64_t s = __hip_atomic_load(w.shared_tau, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_WORKGROUP);
-    // readfirstlane returns int: widen through uint32_t (no sign extension into the high half)
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)s);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(s >> 32));
-    const uint64_t su = ((uint64_t)hi << 32) | lo;
-    if (su > w.tau_key) set_tau(w, su);
+    const uint64_t s = uniform64(__hip_atomic_load(w.shared_tau, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_WORKGROUP));
+    if (s > w.tau_key) set_tau(w, s);
 }
 
-// After a batch that changed the list: publish its n-th key and raise the workgroup threshold to
-// the smallest n-th key over the W waves. Every wave has n distinct elements at or above its
+// After a batch that changed the list: publish its n-th key and raise the unit threshold to the
+// smallest n-th key over the unit's W waves. Every wave has n distinct elements at or above its
 // published key (a list position only ever grows), and W * n >= k, so k real elements reach
 // that minimum: a valid threshold, usually well above the largest single-wave k-th key.
 __device__ __forceinline__ void publish_and_refresh(WaveTopk &w, int lane) {
@@ -103,15 +136,17 @@ __device__ __forceinline__ void publish_and_refresh(WaveTopk &w, int lane) {
     if (mine <= w.pub_mine) return;
     w.pub_mine = mine;
     if (lane == 0)
-        __hip_atomic_store(&w.pub[w.wave], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    // lane v reads wave v's key; the minimum is taken over wave-uniform values (scalar unit)
-    const uint64_t p = lane < w.W ? __hip_atomic_load(&w.pub[lane], __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_WORKGROUP)
-                                  : ~0ull;
+        __hip_atomic_store(&w.pub[w.slot], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    // lane s reads slot s's key; the minimum over the peers is taken on wave-uniform values
+    const uint64_t p = lane < kWaves ? __hip_atomic_load(&w.pub[lane], __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_WORKGROUP)
+                                     : ~0ull;
     uint64_t lo = mine;  // this wave's own value, not a stale read
-    for (int v = 0; v < w.W; ++v) {
-        if (v == w.wave) continue;
-        const uint64_t o = lane_value(p, v);
+    uint32_t others = w.peers & ~(1u << w.slot);
+    while (others != 0u) {
+        const int s = __builtin_ctz(others);
+        others &= others - 1u;
+        const uint64_t o = lane_value(p, s);
         lo = o < lo ? o : lo;
     }
     raise_tau(w, lo, lane);
@@ -127,31 +162,30 @@ __device__ __forceinline__ void wave_insert(WaveTopk &w, uint64_t c, int lane) {
     raise_tau(w, lane_value(w.top, w.k - 1), lane);
 }
 
-// Offer a batch to the wave's top-k. Each lane holds U raw 16-byte vectors in `buf`, of which
+// Offer a batch to the wave's list. Each lane holds U raw 16-byte vectors in `buf`, of which
 // the first NSLOT elements are used; element j of lane L is real only if its vector
-// (j / EV) * 64 + L is below `nvalid` (the raw words of the others may hold anything).
-// `lane_max` is the largest real element of the lane. Element j of lane L has id
+// (j / EV) * 64 + L is below `nvalid` (the raw words of the others may hold anything). `hits`
+// holds every lane that may have an element at or above the threshold (a superset is fine:
+// each element is compared exactly). Element j of lane L has id
 // id_base + L * lane_stride + (j / EV) * 64 * EV + (j % EV).
 template <typename T, int U, int NSLOT>
-__device__ __forceinline__ void offer_lanes(WaveTopk &w, const u32x4 *buf, float lane_max,
-                                            bool lane_ok, int nvalid, int32_t id_base,
-                                            int lane_stride, int lane, u32x4 *xbuf) {
+__device__ __forceinline__ void offer_lanes(WaveTopk &w, const u32x4 *buf, uint64_t hits,
+                                            int nvalid, int32_t id_base, int lane_stride,
+                                            int lane, u32x4 *stage) {
     constexpr int EV = Elem<T>::kPerVec;
     static_assert(NSLOT <= kWave && NSLOT <= U * EV, "one element per lane in the transpose");
-    const bool mine = lane_ok && lane_max >= w.tau_v;
-    uint64_t hits = __ballot(mine);
     if (hits == 0ull) return;
-    if (mine) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) xbuf[lane * U + u] = buf[u];
-    }
-    const int j = lane;  // this lane reads element j of each publishing lane
+    const int j = lane;  // this lane reads element j of each hit lane
     const int vec_j = (j / EV) * kWave;
     while (hits != 0ull) {
         const int L = __builtin_ctzll(hits);
         hits &= hits - 1ull;
+        if (lane == L) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) stage[u] = buf[u];
+        }
         float x = -INFINITY;
-        if (j < NSLOT) x = Elem<T>::lds_element(xbuf, L * U * EV + j);
+        if (j < NSLOT) x = Elem<T>::lds_element(stage, j);
         const bool maybe = j < NSLOT && vec_j + L < nvalid && x >= w.tau_v && x != -INFINITY;
         uint64_t m = __ballot(maybe);
         while (m != 0ull) {
@@ -167,44 +201,24 @@ __device__ __forceinline__ void offer_lanes(WaveTopk &w, const u32x4 *buf, float
     publish_and_refresh(w, lane);
 }
 
-// One lane's online logsumexp update with NB elements (-inf elements add nothing).
-template <int NB>
-__device__ __forceinline__ void lse_update(float &ref, float &sum, const float *x, float bmax) {
-    const float r = fmaxf(ref, bmax * kLog2e);
-    sum *= __builtin_amdgcn_exp2f(ref - r);  // ref = -inf on the first batch: factor 0
-    ref = r;
-#pragma unroll
-    for (int j = 0; j < NB; ++j) sum += __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -r));
-}
-
-// One element, possibly absent (ragged ends and idle lanes).
-__device__ __forceinline__ void lse_update_one(float &ref, float &sum, float x, bool valid) {
-    if (!valid) return;
-    const float r = fmaxf(ref, x * kLog2e);
-    if (ref != r) sum *= __builtin_amdgcn_exp2f(ref - r);
-    ref = r;
-    sum += __builtin_amdgcn_exp2f(fmaf(x, kLog2e, -r));
-}
-
-// U vectors of batch `b`: lane offset `voff` (fixed per lane) plus the wave-uniform batch offset;
-// no per-lane address arithmetic. The descriptor bounds the wave's range: an offset past it
-// reads zeros instead of memory.
-template <int U>
+// Batch `b` of a unit: lane offset `voff` (fixed per lane) plus the wave-uniform batch offset.
+// The descriptor bounds the unit: an offset past it reads zeros instead of memory.
 __device__ __forceinline__ void load_batch(__amdgpu_buffer_rsrc_t rsrc, int voff, int b,
                                            u32x4 *buf) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-        buf[u] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, (b * U + u) * kWave * 16,
+    for (int u = 0; u < kU; ++u)
+        buf[u] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, (b * kU + u) * kWave * 16,
                                                        kNonTemporal);
 }
 
-// Largest element per lane of a batch (only the first `nvalid` vectors are real).
-template <typename T, int U, bool PARTIAL>
+// Elements of a batch and the largest per lane (only the first `nvalid` vectors are real; the
+// others become -inf, which adds nothing to a sum and is never a candidate).
+template <typename T, bool PARTIAL>
 __device__ __forceinline__ void unpack_batch(const u32x4 *buf, int nvalid, int lane, float *x,
                                              float &bmax) {
     constexpr int EV = Elem<T>::kPerVec;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < kU; ++u) {
         Elem<T>::unpack(buf[u], x + u * EV);
         if (PARTIAL && u * kWave + lane >= nvalid) {
 #pragma unroll
@@ -213,207 +227,358 @@ __device__ __forceinline__ void unpack_batch(const u32x4 *buf, int nvalid, int l
     }
     bmax = x[0];
 #pragma unroll
-    for (int j = 1; j < U * EV; ++j) bmax = fmaxf(bmax, x[j]);
+    for (int j = 1; j < kU * EV; ++j) bmax = fmaxf(bmax, x[j]);
 }
 
-// One batch of the wave's range: vectors vbase + lane + u * 64. PARTIAL: only the first
-// `nvalid` vectors are in range; the others (read as zeros) are replaced by -inf, which adds
-// nothing to the sum and is never a candidate.
-template <typename T, int U, bool PARTIAL>
-__device__ __forceinline__ void batch(const u32x4 *buf, int64_t vbase, int64_t g0, int nvalid,
-                                      WaveTopk &w, float &ref, float &sum, int lane,
-                                      u32x4 *xbuf) {
+// One batch: add its terms 2^(x log2e - R) to the lane's chunk sum and offer it to the list.
+// A lane's batch sum is at least its largest term, so a lane whose sum is below the threshold's
+// term (t_e = 2^(tau log2e - R), less a margin for exp2's rounding) holds no candidate, and no
+// lane maximum is needed. When t_e underflows to 0, or the sums flag more than kMaxSumHits lanes
+// (near-flat rows, where every sum is large), the lane maxima decide instead.
+template <typename T, bool PARTIAL>
+__device__ __forceinline__ void batch(const u32x4 *buf, int nvalid, int32_t id_base, float R,
+                                      float t_e, float &csum, WaveTopk &w, int lane,
+                                      u32x4 *stage) {
     constexpr int EV = Elem<T>::kPerVec;
-    constexpr int NB = U * EV;
-    pull_tau(w);
-    float x[NB], bmax;
-    unpack_batch<T, U, PARTIAL>(buf, nvalid, lane, x, bmax);
-    if (!PARTIAL || bmax != -INFINITY) lse_update<NB>(ref, sum, x, bmax);
-    offer_lanes<T, U, (NB < kWave ? NB : kWave)>(w, buf, bmax, bmax != -INFINITY, nvalid,
-                                                  (int32_t)(vbase * EV - g0), EV, lane, xbuf);
-}
-
-// Largest element of each lane over the batches already in the ring (the first NBUF - 1; the
-// batch with index nfull is the partial one, with `tail` vectors). -inf for a lane with no data.
-template <typename T, int U, int NBUF>
-__device__ __forceinline__ float seed_lane_max(const u32x4 (*ring)[U], int nfull, int tail,
-                                               int lane) {
-    float m = -INFINITY;
+    constexpr int NB = kU * EV;
+    float x[NB];
 #pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i) {
-        float x[U * Elem<T>::kPerVec], bmax = -INFINITY;
-        if (i < nfull)
-            unpack_batch<T, U, false>(ring[i], kWave * U, lane, x, bmax);
-        else if (i == nfull && tail > 0)
-            unpack_batch<T, U, true>(ring[i], tail, lane, x, bmax);
-        m = fmaxf(m, bmax);
+    for (int u = 0; u < kU; ++u) {
+        Elem<T>::unpack(buf[u], x + u * EV);
+        if (PARTIAL && u * kWave + lane >= nvalid) {
+#pragma unroll
+            for (int e = 0; e < EV; ++e) x[u * EV + e] = -INFINITY;
+        }
     }
-    return m;
+    float bs = 0.f;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) bs += __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -R));
+    csum += bs;
+    uint64_t hits = __ballot(bs >= t_e);
+    if (t_e == 0.f || __popcll(hits) > kMaxSumHits) {
+        // the sums do not single out a few lanes (e.g. near-flat rows): use the lane maxima
+        float bmax = x[0];
+#pragma unroll
+        for (int j = 1; j < NB; ++j) bmax = fmaxf(bmax, x[j]);
+        hits = __ballot(bmax != -INFINITY && bmax >= w.tau_v);
+    }
+    offer_lanes<T, kU, (NB < kWave ? NB : kWave)>(w, buf, hits, nvalid, id_base, EV, lane, stage);
 }
 
-// The ragged ends of a row (its elements outside whole 16-byte vectors) hold fewer than 2 * EV
-// elements: one per lane. They are loaded before the stream starts and offered after it.
-template <typename T>
-__device__ __forceinline__ float ragged_load(const T *logits, int64_t e0, int64_t e1, int lane) {
-    const int64_t e = e0 + lane;
-    return e < e1 ? Elem<T>::load(logits, e) : -INFINITY;
-}
+// Whole vectors of a unit and its ragged row ends (elements outside whole vectors: the first
+// slice takes the head, the last slice the tail).
+struct UnitRange {
+    int64_t g0;      // first element of the row
+    int64_t c0;      // first whole vector of the unit
+    int nv;          // whole vectors of the unit
+    int64_t h0, h1;  // ragged head [h0, h1)
+    int64_t t0, t1;  // ragged tail [t0, t1)
+};
 
-template <typename T>
-__device__ __forceinline__ void ragged_offer(float x, int64_t e0, int64_t e1, int64_t g0,
-                                             WaveTopk &w, float &ref, float &sum, int lane,
-                                             u32x4 *xbuf) {
-    const bool ok = e0 + lane < e1;
-    lse_update_one(ref, sum, x, ok);
-    const u32x4 raw = Elem<T>::single(x);
-    offer_lanes<T, 1, 1>(w, &raw, x, ok, kWave, (int32_t)(e0 - g0), 1, lane, xbuf);
-}
-
-// Grid: R * S workgroups of W = blockDim.x / 64 waves; workgroup (row, slice) covers part
-// slice of the row, wave w sub-part w of it.
-template <typename T, int U, int NBUF>
-__global__ __launch_bounds__(kWave * kMaxWaves) __attribute__((amdgpu_waves_per_eu(4))) void topk_lse_kernel(
-    const T *__restrict__ logits, int V, int k, int S, int32_t *__restrict__ cand_ids,
-    float *__restrict__ unary, float *__restrict__ lse_out, uint64_t *__restrict__ part_keys,
-    float2 *__restrict__ part_lse) {
-    constexpr int EV = Elem<T>::kPerVec;
-    constexpr int step = U * kWave;  // vectors per batch
-    extern __shared__ __attribute__((aligned(16))) u32x4 xbuf_all[];  // [W][64 * U]
-    __shared__ uint64_t shared_tau;
-    __shared__ float2 wave_lse[kMaxWaves];
-    __shared__ uint32_t seed_vals[kMaxWaves * kWave];
-    __shared__ uint64_t pub[kMaxWaves];
-
-    const int lane = threadIdx.x % kWave;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int W = blockDim.x / kWave;
-    const int64_t row = blockIdx.x / S;
-    const int slice = blockIdx.x % S;
-    u32x4 *xbuf = xbuf_all + wave * (kWave * U);
-
-    if (threadIdx.x == 0) shared_tau = 0ull;  // published to the other waves by the seed barrier
-    if (threadIdx.x < kMaxWaves) pub[threadIdx.x] = 0ull;
-
-    // Whole 16-byte vectors inside this row: [va, vb), split into S * W parts; this wave takes
-    // part slice * W + wave: [c0, c1).
-    const int64_t g0 = row * (int64_t)V, g1 = g0 + V;
-    int64_t va = (g0 + EV - 1) / EV, vb = g1 / EV;
-    if (va > vb) va = vb = 0;
+__device__ __forceinline__ UnitRange unit_range(int64_t unit, int V, int S, int EV) {
+    UnitRange u;
+    const int64_t row = unit / S;
+    const int slice = (int)(unit % S);
+    u.g0 = row * (int64_t)V;
+    const int64_t g1 = u.g0 + V;
+    int64_t va = (u.g0 + EV - 1) / EV, vb = g1 / EV;
+    if (va > vb) va = vb = 0;  // the row lies inside one vector: all of it is ragged
     const int64_t nvec = vb - va;
-    const int parts = S * W, part = slice * W + wave;
-    const int64_t c0 = va + nvec * part / parts, c1 = va + nvec * (part + 1) / parts;
-    const int64_t nv = c1 - c0;
-    const int nfull = (int)(nv / step);
-    const int tail = (int)(nv - (int64_t)nfull * step);  // vectors of the partial last batch
-
-    WaveTopk w;
-    w.top = 0ull;
-    w.tau_key = 0ull;
-    w.tau_v = -INFINITY;
-    w.k = k;
-    w.shared_tau = &shared_tau;
-    w.pub = pub;
-    w.pub_mine = 0ull;
-    w.W = W;
-    w.n = (k + W - 1) / W;
-    w.wave = wave;
-    float ref = -INFINITY, sum = 0.0f;
-
-    // Ragged row ends (the first part takes the head, the last part the tail), loaded up front.
-    const int64_t h0 = g0, h1 = nvec > 0 ? va * EV : g1, t0 = vb * EV, t1 = g1;
-    const bool do_head = part == 0 && h1 > h0;
-    const bool do_tail = part == parts - 1 && nvec > 0 && t1 > t0;
-    const float xh = do_head ? ragged_load<T>(logits, h0, h1, lane) : -INFINITY;
-    const float xt = do_tail ? ragged_load<T>(logits, t0, t1, lane) : -INFINITY;
-
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<u32x4 *>(reinterpret_cast<const u32x4 *>(logits) + c0), 0, (int)(nv * 16),
-        kBufferWord3);
-    const int voff = lane * 16;
-
-    // Batches (the last one partial when tail > 0) go through a ring of NBUF buffers, issued
-    // NBUF - 1 batches ahead of the one processed; all NBUF are in flight during the seed.
-    const int nall = nfull + (tail > 0 ? 1 : 0);
-    u32x4 ring[NBUF][U];
-#pragma unroll
-    for (int i = 0; i < NBUF; ++i)
-        if (i < nall) load_batch<U>(rsrc, voff, i, ring[i]);
-
-    // Threshold seed: the k-th largest of the lane maxima of all waves over their first NBUF - 1
-    // batches (k real elements reach it; -inf, which admits everything, when fewer than k lanes
-    // hold data). The waves' ranges are disjoint, so the maxima are distinct elements. Found as
-    // the largest order-preserving value key t with at least k maxima at or above it, one bit at
-    // a time from the top with ballot counts: no cross-lane data movement.
-    seed_vals[wave * kWave + lane] = value_key(seed_lane_max<T, U, NBUF>(ring, nfull, tail, lane));
-    __syncthreads();
-    {
-        uint32_t v[kMaxWaves];
-#pragma unroll
-        for (int i = 0; i < kMaxWaves; ++i) v[i] = i < W ? seed_vals[i * kWave + lane] : 0u;
-        uint32_t t = 0u;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t c = t | (1u << bit);
-            int n = 0;
-#pragma unroll
-            for (int i = 0; i < kMaxWaves; ++i)
-                if (i < W) n += __popcll(__ballot(v[i] >= c));
-            if (n >= k) t = c;
-        }
-        raise_tau(w, (uint64_t)t << 32, lane);
+    u.c0 = va + nvec * slice / S;
+    u.nv = (int)(va + nvec * (slice + 1) / S - u.c0);
+    u.h0 = u.h1 = u.t0 = u.t1 = 0;
+    if (slice == 0) {
+        u.h0 = u.g0;
+        u.h1 = nvec > 0 ? va * EV : g1;
     }
-
-    for (int b0 = 0; b0 < nfull; b0 += NBUF) {
-#pragma unroll
-        for (int j = 0; j < NBUF; ++j) {
-            const int b = b0 + j;
-            if (b >= nfull) break;
-            if (b >= 1 && b + NBUF - 1 < nall)  // batch NBUF - 1 was loaded before the seed
-                load_batch<U>(rsrc, voff, b + NBUF - 1, ring[(j + NBUF - 1) % NBUF]);
-            batch<T, U, false>(ring[j], c0 + (int64_t)b * step, g0, step, w, ref, sum, lane, xbuf);
-        }
+    if (slice == S - 1 && nvec > 0) {
+        u.t0 = vb * EV;
+        u.t1 = g1;
     }
-    if (tail > 0) {
-        // the partial batch sits in ring slot nfull % NBUF (static register indexing)
-#pragma unroll
-        for (int j = 0; j < NBUF; ++j)
-            if (j == nfull % NBUF)
-                batch<T, U, true>(ring[j], c0 + (int64_t)nfull * step, g0, tail, w, ref, sum,
-                                  lane, xbuf);
-    }
-    if (do_head) ragged_offer<T>(xh, h0, h1, g0, w, ref, sum, lane, xbuf);
-    if (do_tail) ragged_offer<T>(xt, t0, t1, g0, w, ref, sum, lane, xbuf);
+    return u;
+}
 
-    // (ref, sum) across the wave, fixed butterfly order.
+// Unit q and index wv within the unit of wave slot s, mixing the SIMD age classes (slot s sits
+// on SIMD s % 4 with age s / 4) so that every unit gets the same mix; and the inverse.
+template <int G>
+__device__ __forceinline__ void wave_unit(int s, int &q, int &wv) {
+    if (G == 8) {  // pairs of ages (0, 3) and (1, 2)
+        q = s < 8 ? s : 15 - s;
+        wv = s < 8 ? 0 : 1;
+    } else {
+        q = s % G;
+        wv = s / G;
+    }
+}
+template <int G>
+__device__ __forceinline__ int unit_slot(int q, int wv) {
+    if (G == 8) return wv == 0 ? q : 15 - q;
+    return q + G * wv;
+}
+
+// The exact logsumexp pair of a unit's elements with a per-lane online reference (slow path,
+// one wave, used only when a chunk sum left the fast path's range).
+template <typename T>
+__device__ void exact_pair(const T *logits, const UnitRange &u, int lane, float &ref,
+                           float &sum) {
+    constexpr int EV = Elem<T>::kPerVec;
+    ref = -INFINITY;
+    sum = 0.f;
+    auto add = [&](float x) {
+        const float r = fmaxf(ref, x * kLog2e);
+        sum = sum * __builtin_amdgcn_exp2f(ref - r) + __builtin_amdgcn_exp2f(fmaf(x, kLog2e, -r));
+        ref = r;
+    };
+    for (int64_t e = u.h0 + lane; e < u.h1; e += kWave) add(Elem<T>::load(logits, e));
+    for (int64_t e = u.c0 * EV + lane; e < (u.c0 + u.nv) * EV; e += kWave)
+        add(Elem<T>::load(logits, e));
+    for (int64_t e = u.t0 + lane; e < u.t1; e += kWave) add(Elem<T>::load(logits, e));
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) {
         const float oref = __shfl_xor(ref, off, kWave);
         const float osum = __shfl_xor(sum, off, kWave);
         lse_combine(ref, sum, oref, osum);
     }
+}
 
-    // Merge the waves' lists and pairs in wave order (wave 0 merges; lists staged in xbuf).
-    uint64_t *lists = reinterpret_cast<uint64_t *>(xbuf_all);  // [W][64]
-    __syncthreads();  // every wave is done with its xbuf
-    lists[wave * kWave + lane] = w.top;
-    if (lane == 0) wave_lse[wave] = make_float2(ref, sum);
-    __syncthreads();
-    if (wave != 0) return;
-    uint64_t acc = w.top;
-    for (int v = 1; v < W; ++v) {
-        acc = wave_merge_desc(acc, lists[v * kWave + lane], lane);
-        const float2 o = wave_lse[v];
-        lse_combine(ref, sum, o.x, o.y);
+// Grid: ceil(units / G) workgroups of kWaves waves; workgroup g owns units g*G .. g*G + G - 1.
+// Dynamic LDS: the chunk sums [G][nch_max][64] floats.
+template <typename T, int G>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void
+topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, int CB,
+                int nch_max, int32_t *__restrict__ cand_ids, float *__restrict__ unary,
+                float *__restrict__ lse_out, uint64_t *__restrict__ part_keys,
+                float2 *__restrict__ part_lse) {
+    constexpr int EV = Elem<T>::kPerVec;
+    extern __shared__ __attribute__((aligned(16))) float chunk_sums[];
+    __shared__ K1Shared sh;
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    constexpr int W = kWaves / G;
+    int q, wv;
+    wave_unit<G>(wave, q, wv);
+    uint32_t peers = 0u;  // slots of the unit's waves
+#pragma unroll
+    for (int i = 0; i < W; ++i) peers |= 1u << unit_slot<G>(q, i);
+    const int64_t unit = (int64_t)blockIdx.x * G + q;
+    const bool active = unit < n_units;  // trailing units of the last workgroup idle
+    const UnitRange ur = unit_range(active ? unit : 0, V, S, EV);
+    const int nv = active ? ur.nv : 0;
+    const int nb = (nv + kStep - 1) / kStep;  // batches of the unit
+    const int nch = (nb + CB - 1) / CB;       // chunks of the unit
+    const int P = (kRing + CB - 1) / CB;      // chunks per wave assigned up front
+    float *csums = chunk_sums + (size_t)q * nch_max * kWave;
+    u32x4 *stage = sh.stage[wave];
+
+    if (threadIdx.x < kMaxUnits) {
+        sh.tau[threadIdx.x] = 0ull;
+        sh.next_chunk[threadIdx.x] = (uint32_t)(W * P);
+        sh.overflow[threadIdx.x] = 0u;
     }
+    if (threadIdx.x < kWaves) sh.pub[threadIdx.x] = 0ull;
+    // (these reach the other waves through the seed barrier)
+
+    const int voff = lane * 16;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u32x4 *>(reinterpret_cast<const u32x4 *>(logits) + ur.c0), 0, nv * 16,
+        kBufferWord3);
+
+    // Ring slots: data and (wave-uniform) metadata: batch index, chunk, flags (1 valid, 2 first
+    // batch of its chunk, 4 last).
+    u32x4 ring[kRing][kU];
+    int s_b[kRing], s_c[kRing], s_flags[kRing];
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) s_b[j] = s_c[j] = s_flags[j] = 0;
+
+    // Issue side: the chunk being issued and the next batch in it. The wave's first P chunks are
+    // wv, wv + W, ...; later ones come from the unit's counter (which starts at W * P),
+    // requested one chunk ahead. Chunk ids only grow, so every wave runs out of work.
+    int cur_c = 0, cur_i = 0, cur_n = 0, taken = 0;
+    uint32_t pending = 0u;
+    auto take_chunk = [&]() -> int {
+        int c;
+        if (taken < P)
+            c = wv + W * taken;
+        else
+            c = __builtin_amdgcn_readfirstlane(pending);
+        ++taken;
+        if (taken >= P && lane == 0)
+            pending = __hip_atomic_fetch_add(&sh.next_chunk[q], 1u, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_WORKGROUP);
+        return c < nch ? c : -1;
+    };
+    auto issue = [&](int j) {
+        if (cur_i == cur_n) {
+            const int c = take_chunk();
+            if (c < 0) {
+                s_flags[j] = 0;
+                cur_i = cur_n = 0;
+                return;
+            }
+            cur_c = c;
+            cur_i = 0;
+            cur_n = min(CB, nb - c * CB);
+        }
+        const int b = cur_c * CB + cur_i;
+        load_batch(rsrc, voff, b, ring[j]);
+        s_b[j] = b;
+        s_c[j] = cur_c;
+        s_flags[j] = 1 | (cur_i == 0 ? 2 : 0) | (cur_i == cur_n - 1 ? 4 : 0);
+        ++cur_i;
+    };
+
+    // Ragged ends of the unit belong to its wave 0 and are loaded up front.
+    const bool rag_owner = active && wv == 0;
+    float xh = -INFINITY, xt = -INFINITY;
+    if (rag_owner) {
+        if (ur.h0 + lane < ur.h1) xh = Elem<T>::load(logits, ur.h0 + lane);
+        if (ur.t0 + lane < ur.t1) xt = Elem<T>::load(logits, ur.t0 + lane);
+    }
+
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) issue(j);
+
+    // Seed: the lane maxima of the wave's first kRing - 1 batches (and its ragged ends).
+    {
+        float m = fmaxf(xh, xt);
+#pragma unroll
+        for (int j = 0; j < kRing - 1; ++j) {
+            if (s_flags[j] & 1) {
+                float x[kU * EV], bmax;
+                const int nvalid = min(kStep, nv - s_b[j] * kStep);
+                if (nvalid < kStep)
+                    unpack_batch<T, true>(ring[j], nvalid, lane, x, bmax);
+                else
+                    unpack_batch<T, false>(ring[j], kStep, lane, x, bmax);
+                m = fmaxf(m, bmax);
+            }
+        }
+        sh.seed_vals[wave * kWave + lane] = value_key(m);
+    }
+    __syncthreads();
+
+    WaveTopk w;
+    w.top = 0ull;
+    w.k = k;
+    w.shared_tau = &sh.tau[q];
+    w.pub = sh.pub;
+    w.pub_mine = 0ull;
+    w.n = (k + W - 1) / W;
+    w.slot = wave;
+    w.peers = peers;
+    set_tau(w, 0ull);
+    // The unit's threshold is the k-th largest of its waves' maxima (k real elements reach it):
+    // the largest order-preserving value key t with at least k maxima at or above it, found one
+    // bit at a time from the top with ballot counts. Its reference R is the largest maximum.
+    float R;
+    {
+        uint32_t v[W];
+        uint32_t vmax = 0u;
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+            v[i] = sh.seed_vals[unit_slot<G>(q, i) * kWave + lane];
+            vmax = v[i] > vmax ? v[i] : vmax;
+        }
+        uint32_t t = 0u, r = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t c = t | (1u << bit);
+            int n = 0;
+#pragma unroll
+            for (int i = 0; i < W; ++i) n += __popcll(__ballot(v[i] >= c));
+            if (n >= k) t = c;
+            const uint32_t cr = r | (1u << bit);
+            if (__ballot(vmax >= cr) != 0ull) r = cr;
+        }
+        raise_tau(w, (uint64_t)t << 32, lane);
+        R = key_value(r) * kLog2e;
+        if (!(R > -INFINITY)) R = 0.f;  // a unit with no elements
+    }
+
+    // Ragged ends: their own sums, and candidates into this wave's list.
+    if (rag_owner) {
+        float rs = 0.f;
+        if (ur.h0 + lane < ur.h1) rs += __builtin_amdgcn_exp2f(fmaf(xh, kLog2e, -R));
+        if (ur.t0 + lane < ur.t1) rs += __builtin_amdgcn_exp2f(fmaf(xt, kLog2e, -R));
+        sh.rag[q * kWave + lane] = rs;
+        if (__ballot(!(rs <= kSumLimit)) != 0ull && lane == 0) sh.overflow[q] = 1u;
+        u32x4 raw = Elem<T>::single(xh);
+        offer_lanes<T, 1, 1>(w, &raw, __ballot(ur.h0 + lane < ur.h1 && xh >= w.tau_v), kWave,
+                             (int32_t)(ur.h0 - ur.g0), 1, lane, stage);
+        raw = Elem<T>::single(xt);
+        offer_lanes<T, 1, 1>(w, &raw, __ballot(ur.t0 + lane < ur.t1 && xt >= w.tau_v), kWave,
+                             (int32_t)(ur.t0 - ur.g0), 1, lane, stage);
+    }
+
+    // Main loop: process the oldest slot, then issue the next batch into it.
+    float csum = 0.f;
+    const int32_t idb0 = (int32_t)(ur.c0 * EV - ur.g0);
+    bool more = true;
+    while (more) {
+#pragma unroll
+        for (int j = 0; j < kRing; ++j) {
+            if (!(s_flags[j] & 1)) {
+                more = false;
+                break;
+            }
+            pull_tau(w);
+            const float t_e = __builtin_amdgcn_exp2f(fmaf(w.tau_v, kLog2e, -R)) * kTermMargin;
+            if (s_flags[j] & 2) csum = 0.f;
+            const int b = s_b[j];
+            const int nvalid = min(kStep, nv - b * kStep);
+            const int32_t id_base = idb0 + b * kStep * EV;
+            if (nvalid < kStep)
+                batch<T, true>(ring[j], nvalid, id_base, R, t_e, csum, w, lane, stage);
+            else
+                batch<T, false>(ring[j], kStep, id_base, R, t_e, csum, w, lane, stage);
+            if (s_flags[j] & 4) {
+                csums[s_c[j] * kWave + lane] = csum;
+                if (__ballot(!(csum <= kSumLimit)) != 0ull && lane == 0) sh.overflow[q] = 1u;
+            }
+            issue(j);
+        }
+    }
+
+    // Merge each unit's lists: a tree over its waves (index wv absorbs wv + 2^l).
+    sh.lists[wave * kWave + lane] = w.top;
+    __syncthreads();
+    for (int l = 0; (1 << l) < W; ++l) {
+        const bool absorbs = wv % (2 << l) == 0 && wv + (1 << l) < W;
+        if (absorbs) {
+            const int other = unit_slot<G>(q, wv + (1 << l));
+            w.top = wave_merge_desc(w.top, sh.lists[other * kWave + lane], lane);
+        }
+        __syncthreads();
+        if (absorbs) sh.lists[wave * kWave + lane] = w.top;
+        __syncthreads();
+    }
+
+    if (!rag_owner) return;
+    // The unit's logsumexp: chunk sums per lane in chunk order, then the ragged sums, then
+    // across lanes (fixed butterfly); lse = (R + log2 total) ln 2.
+    float ref, sum;
+    if (__hip_atomic_load(&sh.overflow[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u) {
+        float t = 0.f;
+        for (int c = 0; c < nch; ++c) t += csums[c * kWave + lane];
+        t += sh.rag[q * kWave + lane];
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1) t += __shfl_xor(t, off, kWave);
+        ref = R;
+        sum = t;
+    } else {
+        exact_pair<T>(logits, ur, lane, ref, sum);
+    }
+    const uint64_t top = w.top;
     if (S == 1) {
         const double lse = lse_value(ref, sum);
         if (lane < k) {
-            cand_ids[row * k + lane] = key_id(acc);
-            unary[row * k + lane] = (float)((double)key_logit(acc) - lse);
+            cand_ids[unit * k + lane] = key_id(top);
+            unary[unit * k + lane] = (float)((double)key_logit(top) - lse);
         }
-        if (lane == 0 && lse_out) lse_out[row] = (float)lse;
+        if (lane == 0 && lse_out) lse_out[unit] = (float)lse;
     } else {
-        part_keys[(row * S + slice) * kWave + lane] = acc;
-        if (lane == 0) part_lse[row * S + slice] = make_float2(ref, sum);
+        part_keys[unit * kWave + lane] = top;
+        if (lane == 0) part_lse[unit] = make_float2(ref, sum);
     }
 }
 
@@ -438,15 +603,26 @@ __global__ __launch_bounds__(kWave) void topk_merge_kernel(
     if (lane == 0 && lse_out) lse_out[row] = (float)lse;
 }
 
+size_t chunk_sum_bytes(int G, int nch_max) { return (size_t)G * nch_max * kWave * sizeof(float); }
+
 template <typename T>
 hipError_t launch_k1(const TopkPlan &plan, const void *logits, int R, int V, int k,
                      int32_t *cand_ids, float *unary, float *lse, uint64_t *part_keys,
                      float2 *part_lse, hipStream_t stream) {
-    const dim3 grid((unsigned)(R * plan.slices)), block(kWave * plan.waves);
-    const size_t lds = (size_t)plan.waves * kWave * kU * sizeof(u32x4);
-    hipLaunchKernelGGL((topk_lse_kernel<T, kU, kRing>), grid, block, lds, stream,
-                       static_cast<const T *>(logits), V, k, plan.slices, cand_ids, unary, lse,
-                       part_keys, part_lse);
+    const int units = R * plan.slices;
+    const dim3 grid((unsigned)((units + plan.groups - 1) / plan.groups)), block(kThreads);
+    const size_t lds = chunk_sum_bytes(plan.groups, plan.chunks);
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, block, lds, stream, static_cast<const T *>(logits), V, k,
+                           plan.slices, units, plan.chunk_batches, plan.chunks, cand_ids, unary,
+                           lse, part_keys, part_lse);
+    };
+    switch (plan.groups) {
+    case 1: go(topk_lse_kernel<T, 1>); break;
+    case 2: go(topk_lse_kernel<T, 2>); break;
+    case 4: go(topk_lse_kernel<T, 4>); break;
+    default: go(topk_lse_kernel<T, 8>); break;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.slices == 1) return e;
     hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)R), dim3(kWave), 0, stream, k,
@@ -457,21 +633,34 @@ hipError_t launch_k1(const TopkPlan &plan, const void *logits, int R, int V, int
 }  // namespace
 
 TopkPlan plan_topk(int R, int V, int elem_bytes) {
-    // About 4096 waves (16 per CU, 4 per SIMD), each streaming at least 2 batches: as many waves
-    // per row as that allows (up to kMaxWaves in one workgroup), then slices if rows are still too few.
-    const int64_t target_waves = 4096;
-    const int64_t batch_elems = (int64_t)kWave * kU * (16 / elem_bytes);
-    int64_t max_parts = (int64_t)V / (batch_elems * 2);
-    if (max_parts < 1) max_parts = 1;
-    int64_t want = (target_waves + R - 1) / R;
-    if (want > max_parts) want = max_parts;
-    if (want < 1) want = 1;
+    const int64_t EV = 16 / elem_bytes;
+    const int64_t nvec_row = V / EV + 1;  // whole vectors of a row, rounded up
+    const int64_t nb_row = (nvec_row + kStep - 1) / kStep;
     TopkPlan p;
-    p.waves = 1;
-    while (p.waves * 2 <= want && p.waves * 2 <= kMaxWaves) p.waves *= 2;
-    p.slices = (int)((want + p.waves - 1) / p.waves);
-    if ((int64_t)p.slices * p.waves > max_parts) p.slices = (int)(max_parts / p.waves);
-    if (p.slices < 1) p.slices = 1;
+    // Slices only when rows are fewer than workgroups, and never below kMinBatchesPerWave
+    // batches per wave.
+    int64_t s = 1;
+    if (R < kTargetWorkgroups) {
+        s = (kTargetWorkgroups + R - 1) / R;
+        const int64_t s_max = nb_row / ((int64_t)kWaves * kMinBatchesPerWave);
+        if (s > s_max) s = s_max;
+        if (s < 1) s = 1;
+    }
+    p.slices = (int)s;
+    const int64_t units = (int64_t)R * p.slices;
+    p.groups = 1;
+    while (p.groups * 2 <= kMaxUnits &&
+           (units + p.groups * 2 - 1) / (p.groups * 2) >= kTargetWorkgroups)
+        p.groups *= 2;
+    p.waves = kWaves / p.groups;
+    const int64_t nb_unit = (nvec_row / p.slices + 1 + kStep - 1) / kStep;  // slices differ by <= 1
+    p.chunk_batches = 1;
+    for (;;) {
+        p.chunks = (int)((nb_unit + p.chunk_batches - 1) / p.chunk_batches);
+        if (p.chunks < 1) p.chunks = 1;
+        if (chunk_sum_bytes(p.groups, p.chunks) <= kLdsBudget) break;
+        p.chunk_batches *= 2;
+    }
     return p;
 }
 

@@ -68,6 +68,14 @@ def _logits(case, R, V, dtype, seed):
     elif case == "peaked":
         x = rng.normal(0, 0.1, (R, V))
         x[np.arange(R), rng.integers(0, V, R)] += 12.0
+    elif case == "high":  # exp(x) beyond fp32 range: the exact logsumexp path
+        x = rng.normal(75, 2, (R, V))
+    elif case == "low":  # exp(x) below fp32 normal range
+        x = rng.normal(-80, 2, (R, V))
+    elif case == "mixed_range":  # rows alternate between ordinary, high and low logits
+        x = rng.normal(0, 3, (R, V)) + np.array([0.0, 90.0, -95.0])[np.arange(R) % 3][:, None]
+    elif case == "wide":  # one row spanning a huge range: a few terms overflow
+        x = rng.uniform(-300, 300, (R, V))
     else:
         raise ValueError(case)
     return store(x.astype(np.float32), dtype)
@@ -93,6 +101,12 @@ TOPK_CASES = [
     ("ascending", 2, 20000, 16, "f32"),
     ("descending", 2, 20000, 16, "bf16"),
     ("peaked", 64, 151936, 32, "f32"),
+    ("high", 5, 70001, 16, "f32"),
+    ("high", 4, 151936, 16, "bf16"),
+    ("low", 5, 70001, 16, "bf16"),
+    ("mixed_range", 24, 40000, 16, "f32"),
+    ("mixed_range", 1030, 3000, 8, "bf16"),
+    ("wide", 3, 50000, 64, "f32"),
 ]
 
 
