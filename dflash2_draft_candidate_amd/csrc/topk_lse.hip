@@ -53,6 +53,7 @@ constexpr size_t kLdsBudget = 120 * 1024; // dynamic LDS (chunk sums) per workgr
 constexpr float kSumLimit = 0x1p100f;     // a chunk sum above this leaves the fast path
 constexpr float kTermMargin = 1.f - 0x1p-10f;  // v_exp_f32 is far more accurate than this
 constexpr int kMaxSumHits = 4;            // lanes the sum filter may flag before maxima decide
+constexpr int kQueue = 64;                // candidate queue slots per unit
 constexpr int kBufferWord3 = 0x00020000;  // gfx9-family buffer descriptor word 3 (raw data)
 constexpr int kNonTemporal = 2;           // cache policy: streaming data, read once
 constexpr int kDppWaveShr1 = 0x138;       // DPP control: lane i reads lane i - 1
@@ -83,8 +84,11 @@ __device__ __forceinline__ uint64_t shift_up_one(uint64_t v) {
 // Per-workgroup state in LDS (besides the chunk sums).
 struct K1Shared {
     uint64_t tau[kMaxUnits];          // admission threshold of each unit
-    uint64_t pub[kWaves];             // per wave: its list's n-th key (n = ceil(k / W))
-    uint64_t lists[kWaves * kWave];   // the waves' lists, for the final merge
+    uint64_t queue[kMaxUnits][kQueue];  // candidates on their way to the unit's owner (0: empty)
+    uint32_t q_tail[kMaxUnits];       // queue slots reserved so far
+    uint32_t q_head[kMaxUnits];       // queue slots consumed by the owner so far
+    uint32_t spilled;                 // bit s: slot s kept candidates in its own list
+    uint64_t lists[kWaves * kWave];   // spilled lists, for the final merge
     uint32_t seed_vals[kWaves * kWave];
     float rag[kMaxUnits * kWave];     // the unit's ragged-end sums per lane
     u32x4 stage[kWaves][kU];          // per wave: one hit lane's batch, read back transposed
@@ -93,16 +97,17 @@ struct K1Shared {
 };
 
 struct WaveTopk {
-    uint64_t top;          // this lane's entry of the wave's sorted list (lane = rank)
+    uint64_t top;          // this lane's entry of the wave's sorted list (lane = rank): the
+                           // unit's list for its owner, an overflow list for the others
     uint64_t tau_key;      // admission threshold (wave-uniform): a key must exceed it
     float tau_v;           // logit of the threshold, for the cheap first test
     int k;
     uint64_t *shared_tau;  // the unit's threshold in LDS
-    uint64_t *pub;         // the unit's published keys, indexed by wave slot
-    uint64_t pub_mine;     // what this wave last published
-    int n;                 // ceil(k / W)
-    int slot;              // this wave's slot in the workgroup
-    uint32_t peers;        // bit s: slot s streams the same unit
+    uint64_t *queue;       // the unit's candidate queue
+    uint32_t *q_tail, *q_head;
+    uint32_t head;         // owner: slots consumed
+    bool owner;            // this wave keeps the unit's list
+    bool spilled;          // a non-owner that had to keep candidates itself
 };
 
 __device__ __forceinline__ void set_tau(WaveTopk &w, uint64_t key) {
@@ -127,31 +132,6 @@ __device__ __forceinline__ void pull_tau(WaveTopk &w) {
     if (s > w.tau_key) set_tau(w, s);
 }
 
-// After a batch that changed the list: publish its n-th key and raise the unit threshold to the
-// smallest n-th key over the unit's W waves. Every wave has n distinct elements at or above its
-// published key (a list position only ever grows), and W * n >= k, so k real elements reach
-// that minimum: a valid threshold, usually well above the largest single-wave k-th key.
-__device__ __forceinline__ void publish_and_refresh(WaveTopk &w, int lane) {
-    const uint64_t mine = lane_value(w.top, w.n - 1);
-    if (mine <= w.pub_mine) return;
-    w.pub_mine = mine;
-    if (lane == 0)
-        __hip_atomic_store(&w.pub[w.slot], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    // lane s reads slot s's key; the minimum over the peers is taken on wave-uniform values
-    const uint64_t p = lane < kWaves ? __hip_atomic_load(&w.pub[lane], __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_WORKGROUP)
-                                     : ~0ull;
-    uint64_t lo = mine;  // this wave's own value, not a stale read
-    uint32_t others = w.peers & ~(1u << w.slot);
-    while (others != 0u) {
-        const int s = __builtin_ctz(others);
-        others &= others - 1u;
-        const uint64_t o = lane_value(p, s);
-        lo = o < lo ? o : lo;
-    }
-    raise_tau(w, lo, lane);
-}
-
 // Insert key c (wave-uniform, above the threshold) into the sorted list: its rank is the number
 // of larger entries (a ballot), entries from that rank on move down one lane, and the threshold
 // follows the wave's k-th key once k entries exist.
@@ -160,6 +140,65 @@ __device__ __forceinline__ void wave_insert(WaveTopk &w, uint64_t c, int lane) {
     const uint64_t prev = shift_up_one(w.top);
     w.top = lane < p ? w.top : (lane == p ? c : prev);
     raise_tau(w, lane_value(w.top, w.k - 1), lane);
+}
+
+// A candidate above the threshold: the owner inserts it; another wave queues it for the owner,
+// or, if the queue is full, keeps it in its own list (merged at the end). Queueing never waits.
+__device__ __forceinline__ void accept(WaveTopk &w, uint64_t c, int lane) {
+    if (w.owner) {
+        wave_insert(w, c, lane);
+        return;
+    }
+    uint32_t pos = 0u;
+    if (lane == 0)
+        pos = __hip_atomic_fetch_add(w.q_tail, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    pos = __builtin_amdgcn_readfirstlane(pos);
+    const uint32_t head = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(w.q_head, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+    if (pos - head < (uint32_t)kQueue) {  // the slot's previous occupant has been consumed
+        if (lane == 0)
+            __hip_atomic_store(&w.queue[pos % kQueue], c, __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else {  // full (the reserved slot stays 0, a hole the owner skips at the end)
+        wave_insert(w, c, lane);
+        w.spilled = true;
+    }
+}
+
+// Owner: insert the queued candidates, consuming the written prefix of the queue (a reserved
+// slot not yet written stops it until the next call). `all`: after the stream, when every
+// reserved slot is final: take every written slot and skip holes.
+__device__ __forceinline__ void drain(WaveTopk &w, int lane, bool all) {
+    const uint32_t tail = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(w.q_tail, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+    while (w.head != tail) {
+        const uint32_t n = min(tail - w.head, (uint32_t)kWave);
+        const uint32_t slot = (w.head + lane) % kQueue;
+        const uint64_t key = lane < (int)n ? __hip_atomic_load(&w.queue[slot], __ATOMIC_ACQUIRE,
+                                                               __HIP_MEMORY_SCOPE_WORKGROUP)
+                                           : 0ull;
+        const uint64_t written = __ballot(key != 0ull);
+        uint32_t cnt = n;
+        if (!all) {  // the prefix of written slots
+            const uint64_t gaps = ~written & (n >= 64 ? ~0ull : ((1ull << n) - 1ull));
+            cnt = gaps ? (uint32_t)__builtin_ctzll(gaps) : n;
+        }
+        if (cnt == 0u) return;
+        uint64_t m = written & (cnt >= 64 ? ~0ull : ((1ull << cnt) - 1ull));
+        while (m != 0ull) {
+            const int src = __builtin_ctzll(m);
+            m &= m - 1ull;
+            const uint64_t c = lane_value(key, src);
+            if (c > w.tau_key) wave_insert(w, c, lane);
+        }
+        if (lane < (int)cnt)
+            __hip_atomic_store(&w.queue[slot], 0ull, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+        w.head += cnt;
+        if (lane == 0)
+            __hip_atomic_store(w.q_head, w.head, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (cnt < n) return;
+    }
 }
 
 // Offer a batch to the wave's list. Each lane holds U raw 16-byte vectors in `buf`, of which
@@ -195,10 +234,9 @@ __device__ __forceinline__ void offer_lanes(WaveTopk &w, const u32x4 *buf, uint6
             const float xs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), src));
             const int32_t id = id_base + L * lane_stride + (src / EV) * kWave * EV + (src % EV);
             const uint64_t c = cand_key(xs, id);
-            if (c > w.tau_key) wave_insert(w, c, lane);
+            if (c > w.tau_key) accept(w, c, lane);
         }
     }
-    publish_and_refresh(w, lane);
 }
 
 // Batch `b` of a unit: lane offset `voff` (fixed per lane) plus the wave-uniform batch offset.
@@ -376,7 +414,9 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
         sh.next_chunk[threadIdx.x] = (uint32_t)(W * P);
         sh.overflow[threadIdx.x] = 0u;
     }
-    if (threadIdx.x < kWaves) sh.pub[threadIdx.x] = 0ull;
+    if (threadIdx.x < kMaxUnits) sh.q_tail[threadIdx.x] = sh.q_head[threadIdx.x] = 0u;
+    if (threadIdx.x == 0) sh.spilled = 0u;
+    for (int i = threadIdx.x; i < kMaxUnits * kQueue; i += kThreads) (&sh.queue[0][0])[i] = 0ull;
     // (these reach the other waves through the seed barrier)
 
     const int voff = lane * 16;
@@ -462,11 +502,12 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     w.top = 0ull;
     w.k = k;
     w.shared_tau = &sh.tau[q];
-    w.pub = sh.pub;
-    w.pub_mine = 0ull;
-    w.n = (k + W - 1) / W;
-    w.slot = wave;
-    w.peers = peers;
+    w.queue = sh.queue[q];
+    w.q_tail = &sh.q_tail[q];
+    w.q_head = &sh.q_head[q];
+    w.head = 0u;
+    w.owner = active && wv == 0;  // the unit's oldest wave keeps its list
+    w.spilled = false;
     set_tau(w, 0ull);
     // The unit's threshold is the k-th largest of its waves' maxima (k real elements reach it):
     // the largest order-preserving value key t with at least k maxima at or above it, found one
@@ -521,6 +562,7 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
                 more = false;
                 break;
             }
+            if (w.owner) drain(w, lane, false);
             pull_tau(w);
             const float t_e = __builtin_amdgcn_exp2f(fmaf(w.tau_v, kLog2e, -R)) * kTermMargin;
             if (s_flags[j] & 2) csum = 0.f;
@@ -539,21 +581,24 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
         }
     }
 
-    // Merge each unit's lists: a tree over its waves (index wv absorbs wv + 2^l).
-    sh.lists[wave * kWave + lane] = w.top;
+    // Every wave is done, so every reserved queue slot is final: the owner takes what is left in
+    // the queue and merges the lists of any wave that had to keep candidates itself.
     __syncthreads();
-    for (int l = 0; (1 << l) < W; ++l) {
-        const bool absorbs = wv % (2 << l) == 0 && wv + (1 << l) < W;
-        if (absorbs) {
-            const int other = unit_slot<G>(q, wv + (1 << l));
-            w.top = wave_merge_desc(w.top, sh.lists[other * kWave + lane], lane);
-        }
-        __syncthreads();
-        if (absorbs) sh.lists[wave * kWave + lane] = w.top;
-        __syncthreads();
+    if (w.spilled) {
+        sh.lists[wave * kWave + lane] = w.top;
+        if (lane == 0)
+            __hip_atomic_fetch_or(&sh.spilled, 1u << wave, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-
+    __syncthreads();
     if (!rag_owner) return;
+    drain(w, lane, true);
+    uint32_t sp = sh.spilled & peers;
+    while (sp != 0u) {
+        const int s = __builtin_ctz(sp);
+        sp &= sp - 1u;
+        w.top = wave_merge_desc(w.top, sh.lists[s * kWave + lane], lane);
+    }
     // The unit's logsumexp: chunk sums per lane in chunk order, then the ragged sums, then
     // across lanes (fixed butterfly); lse = (R + log2 total) ln 2.
     float ref, sum;
