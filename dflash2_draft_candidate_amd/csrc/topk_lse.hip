@@ -54,6 +54,7 @@ constexpr float kSumLimit = 0x1p100f;     // a chunk sum above this leaves the f
 constexpr float kTermMargin = 1.f - 0x1p-10f;  // v_exp_f32 is far more accurate than this
 constexpr int kMaxSumHits = 4;            // lanes the sum filter may flag before maxima decide
 constexpr int kQueue = 64;                // candidate queue slots per unit
+constexpr int kSeedBatches = 3;           // batches per wave behind the seed (<= kRing)
 constexpr int kBufferWord3 = 0x00020000;  // gfx9-family buffer descriptor word 3 (raw data)
 constexpr int kNonTemporal = 2;           // cache policy: streaming data, read once
 constexpr int kDppWaveShr1 = 0x138;       // DPP control: lane i reads lane i - 1
@@ -479,11 +480,11 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
 #pragma unroll
     for (int j = 0; j < kRing; ++j) issue(j);
 
-    // Seed: the lane maxima of the wave's first kRing - 1 batches (and its ragged ends).
+    // Seed: the lane maxima of the wave's first kSeedBatches batches (and its ragged ends).
     {
         float m = fmaxf(xh, xt);
 #pragma unroll
-        for (int j = 0; j < kRing - 1; ++j) {
+        for (int j = 0; j < kSeedBatches; ++j) {
             if (s_flags[j] & 1) {
                 float x[kU * EV], bmax;
                 const int nvalid = min(kStep, nv - s_b[j] * kStep);
