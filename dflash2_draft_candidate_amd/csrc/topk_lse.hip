@@ -289,9 +289,9 @@ __device__ __forceinline__ void batch(const u32x4 *buf, int nvalid, int32_t id_b
             for (int e = 0; e < EV; ++e) x[u * EV + e] = -INFINITY;
         }
     }
-    float bs = 0.f;
+    float bs = __builtin_amdgcn_exp2f(fmaf(x[0], kLog2e, -R));
 #pragma unroll
-    for (int j = 0; j < NB; ++j) bs += __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -R));
+    for (int j = 1; j < NB; ++j) bs += __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -R));
     csum += bs;
     uint64_t hits = __ballot(bs >= t_e);
     if (t_e == 0.f || __popcll(hits) > kMaxSumHits) {
@@ -555,6 +555,8 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     // Main loop: process the oldest slot, then issue the next batch into it.
     float csum = 0.f;
     const int32_t idb0 = (int32_t)(ur.c0 * EV - ur.g0);
+    uint64_t te_key = ~0ull;  // the threshold t_e was computed for
+    float t_e = 0.f;
     bool more = true;
     while (more) {
 #pragma unroll
@@ -565,7 +567,10 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
             }
             if (w.owner) drain(w, lane, false);
             pull_tau(w);
-            const float t_e = __builtin_amdgcn_exp2f(fmaf(w.tau_v, kLog2e, -R)) * kTermMargin;
+            if (w.tau_key != te_key) {  // the threshold's term, recomputed only when it moved
+                te_key = w.tau_key;
+                t_e = __builtin_amdgcn_exp2f(fmaf(w.tau_v, kLog2e, -R)) * kTermMargin;
+            }
             if (s_flags[j] & 2) csum = 0.f;
             const int b = s_b[j];
             const int nvalid = min(kStep, nv - b * kStep);
