@@ -51,6 +51,7 @@ constexpr int kTargetWorkgroups = 256;    // one per CU
 constexpr int kMinBatchesPerWave = 2;     // slices are not cut smaller than this per wave
 constexpr size_t kLdsBudget = 120 * 1024; // dynamic LDS (chunk sums) per workgroup
 constexpr float kSumLimit = 0x1p100f;     // a chunk sum above this leaves the fast path
+constexpr float kSumFloor = 0x1p-60f;     // so does a unit total below this
 constexpr float kTermMargin = 1.f - 0x1p-10f;  // v_exp_f32 is far more accurate than this
 constexpr int kMaxSumHits = 4;            // lanes the sum filter may flag before maxima decide
 constexpr int kQueue = 64;                // candidate queue slots per unit
@@ -94,6 +95,7 @@ struct K1Shared {
     float rag[kMaxUnits * kWave];     // the unit's ragged-end sums per lane
     u32x4 stage[kWaves][kU];          // per wave: one hit lane's batch, read back transposed
     uint32_t next_chunk[kMaxUnits];   // next chunk of the unit to hand out
+    uint32_t seeded[kMaxUnits];       // waves of the unit that have published their seed
     uint32_t overflow[kMaxUnits];     // a chunk sum left the safe range
 };
 
@@ -418,7 +420,8 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     if (threadIdx.x < kMaxUnits) sh.q_tail[threadIdx.x] = sh.q_head[threadIdx.x] = 0u;
     if (threadIdx.x == 0) sh.spilled = 0u;
     for (int i = threadIdx.x; i < kMaxUnits * kQueue; i += kThreads) (&sh.queue[0][0])[i] = 0ull;
-    // (these reach the other waves through the seed barrier)
+    if (threadIdx.x < kMaxUnits) sh.seeded[threadIdx.x] = 0u;
+    __syncthreads();  // the only barrier before the stream (every wave arrives long before data)
 
     const int voff = lane * 16;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -497,7 +500,6 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
         }
         sh.seed_vals[wave * kWave + lane] = value_key(m);
     }
-    __syncthreads();
 
     WaveTopk w;
     w.top = 0ull;
@@ -510,32 +512,42 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     w.owner = active && wv == 0;  // the unit's oldest wave keeps its list
     w.spilled = false;
     set_tau(w, 0ull);
-    // The unit's threshold is the k-th largest of its waves' maxima (k real elements reach it):
-    // the largest order-preserving value key t with at least k maxima at or above it, found one
-    // bit at a time from the top with ballot counts. Its reference R is the largest maximum.
-    float R;
-    {
-        uint32_t v[W];
-        uint32_t vmax = 0u;
-#pragma unroll
-        for (int i = 0; i < W; ++i) {
-            v[i] = sh.seed_vals[unit_slot<G>(q, i) * kWave + lane];
-            vmax = v[i] > vmax ? v[i] : vmax;
-        }
-        uint32_t t = 0u, r = 0u;
+    // Threshold seed, with no barrier: the wave starts from the k-th largest of its own 64 lane
+    // maxima, then publishes them; the unit's last wave to publish raises the unit threshold to
+    // the k-th largest of all of them. Either has k real elements at or above it. The k-th
+    // largest of a set of order-preserving value keys is the largest t with at least k keys at
+    // or above it, found one bit at a time from the top with ballot counts.
+    if (active) {
+        const uint32_t mk = sh.seed_vals[wave * kWave + lane];
+        uint32_t t = 0u;
         for (int bit = 31; bit >= 0; --bit) {
             const uint32_t c = t | (1u << bit);
-            int n = 0;
-#pragma unroll
-            for (int i = 0; i < W; ++i) n += __popcll(__ballot(v[i] >= c));
-            if (n >= k) t = c;
-            const uint32_t cr = r | (1u << bit);
-            if (__ballot(vmax >= cr) != 0ull) r = cr;
+            if (__popcll(__ballot(mk >= c)) >= k) t = c;
         }
         raise_tau(w, (uint64_t)t << 32, lane);
-        R = key_value(r) * kLog2e;
-        if (!(R > -INFINITY)) R = 0.f;  // a unit with no elements
+        uint32_t arrived = 0u;
+        if (lane == 0)
+            arrived = __hip_atomic_fetch_add(&sh.seeded[q], 1u, __ATOMIC_ACQ_REL,
+                                             __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (__builtin_amdgcn_readfirstlane(arrived) == W - 1) {
+            // the last of the unit to arrive: every peer's maxima are in LDS
+            uint32_t v[W];
+#pragma unroll
+            for (int i = 0; i < W; ++i) v[i] = sh.seed_vals[unit_slot<G>(q, i) * kWave + lane];
+            uint32_t u = 0u;
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t c = u | (1u << bit);
+                int n = 0;
+#pragma unroll
+                for (int i = 0; i < W; ++i) n += __popcll(__ballot(v[i] >= c));
+                if (n >= k) u = c;
+            }
+            raise_tau(w, (uint64_t)u << 32, lane);
+        }
     }
+    // logsumexp reference, fixed for every unit: terms are 2^(x log2e). Rows whose terms leave
+    // fp32's range go down the exact path at the end.
+    constexpr float R = 0.f;
 
     // Ragged ends: their own sums, and candidates into this wave's list.
     if (rag_owner) {
@@ -607,16 +619,19 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     }
     // The unit's logsumexp: chunk sums per lane in chunk order, then the ragged sums, then
     // across lanes (fixed butterfly); lse = (R + log2 total) ln 2.
-    float ref, sum;
-    if (__hip_atomic_load(&sh.overflow[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u) {
+    float ref = R, sum = 0.f;
+    bool fast =
+        __hip_atomic_load(&sh.overflow[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u;
+    if (fast) {
         float t = 0.f;
         for (int c = 0; c < nch; ++c) t += csums[c * kWave + lane];
         t += sh.rag[q * kWave + lane];
 #pragma unroll
         for (int off = kWave / 2; off > 0; off >>= 1) t += __shfl_xor(t, off, kWave);
-        ref = R;
         sum = t;
-    } else {
+        fast = t >= kSumFloor;  // every term far below 1: too few significant bits left
+    }
+    if (!fast) {
         exact_pair<T>(logits, ur, lane, ref, sum);
     }
     const uint64_t top = w.top;
