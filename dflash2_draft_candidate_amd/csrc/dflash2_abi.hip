@@ -42,6 +42,7 @@ struct SelectLayout {
 };
 
 // Workspace of dflash2_select: lse [R] | gate partials [splits][R][r] | K1 slice partials.
+// (The fused gate uses at most gate_splits splits.)
 SelectLayout select_layout(int R, int V, int H, int r, int logits_dtype, int act_dtype) {
     SelectLayout s;
     size_t off = 0;
@@ -179,13 +180,30 @@ int dflash2_select(const void *logits, int logits_dtype, const void *hidden, int
     float *gpart = reinterpret_cast<float *>(ws + lay.gpart);
     hipStream_t s = static_cast<hipStream_t>(stream);
 
-    hipError_t e = launch_topk_lse(logits, logits_dtype, R, V, k, cand_ids, unary, lse,
-                                   ws + lay.topk, s);
-    if (e == hipSuccess)
-        e = launch_gate_partials(hidden, W_sel, act_dtype, R, H, r, gpart, s);
-    if (e == hipSuccess)
-        e = launch_lattice(cand_ids, unary, gpart, gate_splits(R, H, act_dtype), pred_cb, succ_cb,
-                           cb_dtype, anchor_ids, B, L, V, r, k, edges, s);
+    // bf16 activations: the top-k pass carries the gate product (r <= 128); otherwise the gate
+    // kernel runs on its own.
+    const int fused = act_dtype == DFLASH2_BF16 ? fused_gate_splits(R, V, logits_dtype, H, r) : 0;
+    hipError_t e;
+    int ksplit;
+    if (fused > 0) {
+        const FusedGate fg{hidden, W_sel, H, r, gpart};
+        e = launch_topk_lse(logits, logits_dtype, R, V, k, cand_ids, unary, lse, ws + lay.topk, s,
+                            &fg);
+        ksplit = fused;
+    } else {
+        e = launch_topk_lse(logits, logits_dtype, R, V, k, cand_ids, unary, lse, ws + lay.topk, s);
+        if (e == hipSuccess) e = launch_gate_partials(hidden, W_sel, act_dtype, R, H, r, gpart, s);
+        ksplit = gate_splits(R, H, act_dtype);
+    }
+    if (e != hipSuccess) return hip_status(e);
+    // Short blocks: lattice and walk in one kernel (one workgroup per sequence); long blocks
+    // spread the lattice over more workgroups and walk in a second kernel.
+    if (lattice_walk_fits(L, k))
+        return hip_status(launch_lattice_walk(cand_ids, unary, gpart, ksplit, pred_cb, succ_cb,
+                                              cb_dtype, anchor_ids, B, L, V, r, k, edges, path,
+                                              nullptr, s));
+    e = launch_lattice(cand_ids, unary, gpart, ksplit, pred_cb, succ_cb, cb_dtype, anchor_ids, B,
+                       L, V, r, k, edges, s);
     if (e == hipSuccess) e = launch_walk(edges, cand_ids, B, L, k, path, nullptr, s);
     return hip_status(e);
 }

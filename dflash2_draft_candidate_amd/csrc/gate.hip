@@ -5,157 +5,41 @@
 // llama.cpp" (ramgpt.org), section "What llama.cpp Actually Builds for the Selector" (the current
 // hidden state projected through the selector-hidden weight). Read here as a plain linear map.
 //
-// bf16 inputs run on the gfx950 matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
-// The product is skinny (r <= 256 columns) and HBM-bound on reading `hidden`, so the kernel is
-// built for independent loads in flight, with no LDS staging and no barriers in the main loop:
+// bf16 inputs run on the gfx950 matrix cores (gate_tile.h: v_mfma_f32_16x16x32_bf16, fp32
+// accumulation). The product is skinny (r <= 256 columns) and HBM-bound on reading `hidden`, so
+// the kernel is built for independent loads in flight, with no LDS staging and no barriers in
+// the main loop:
 //   * a wave owns 16 rows and a range of H; the 4 waves of a workgroup split one range 4 ways
 //     and are summed through LDS at the end; `splits` workgroups cover H;
-//   * A fragments (8 consecutive h of one row) are 16-byte loads of `hidden`;
-//   * W_sel is [H, r] (r contiguous), but a B fragment needs 8 consecutive h of one column. Each
-//     lane loads 4-byte column pairs (2c, 2c+1) of its 8 rows of W_sel and repacks the low halves
-//     into the fragment of one output tile and the high halves into the next, so the output
-//     columns of tile pair (2p, 2p+1) at lane position m are 32p + 2m and 32p + 2m + 1. Every
-//     load is independent: a batch of steps is issued before any MFMA runs;
 //   * each split writes its own partial [R, r] tile; the lattice kernel (or, for the stand-alone
 //     gate, a reduction kernel) sums the splits in split order: deterministic, no atomics.
+// The top-k kernel can compute the same tiles itself (one per workgroup, before it streams);
+// the results are identical, since the waves' ranges and the summation order are the same.
 // fp32 inputs use a plain fp32 FMA kernel that writes g directly.
 #include "device_common.h"
+#include "gate_tile.h"
 #include "kernels.h"
 
 namespace dflash2 {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kGateWaves = 4;
 constexpr int kGateThreads = kGateWaves * kWave;
-constexpr int kStepK = 32;  // H per MFMA
 constexpr int kTargetWgs = 256;
-
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
-
-// Output column of MFMA tile t at lane position m (NT >= 2: column pairs; NT == 1: identity).
-template <int NT>
-__device__ __forceinline__ int out_col(int t, int m) {
-    return NT == 1 ? m : 32 * (t >> 1) + 2 * m + (t & 1);
-}
-
-template <int NT>
-struct Step {
-    static constexpr int NP = NT == 1 ? 1 : NT / 2;  // column pairs per lane
-    u32x4 a;                                        // A fragment
-    uint32_t w[8][NP];                              // W rows k0+8g+i, column pair p
-};
-
-// Loads of one 32-wide step. FAST (wave-uniform): the step lies inside H, H % 8 == 0 and r is
-// exactly the padded tile width, so every load is unconditional (rows past R read row R-1 and
-// are discarded at the store); no branch separates the loads, and they all stay in flight.
-template <int NT, bool FAST>
-__device__ __forceinline__ void load_step(Step<NT> &s, const uint16_t *hrow, bool row_ok,
-                                          const uint16_t *W, int H, int r, int k0, int g, int m) {
-    const int kc = k0 + 8 * g;
-    if (FAST) {
-        s.a = *reinterpret_cast<const u32x4 *>(hrow + kc);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint16_t *wrow = W + (int64_t)(kc + i) * r;
-#pragma unroll
-            for (int p = 0; p < Step<NT>::NP; ++p)
-                s.w[i][p] = NT == 1 ? (uint32_t)wrow[m]
-                                    : *reinterpret_cast<const uint32_t *>(wrow + 32 * p + 2 * m);
-        }
-        return;
-    }
-    uint32_t v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (row_ok && kc + i < H) ? hrow[kc + i] : 0u;
-    s.a = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int kr = kc + i;
-        const uint16_t *wrow = W + (int64_t)kr * r;
-#pragma unroll
-        for (int p = 0; p < Step<NT>::NP; ++p) {
-            if (NT == 1) {
-                s.w[i][p] = (kr < H && m < r) ? wrow[m] : 0u;
-            } else {
-                const int c = 32 * p + 2 * m;
-                s.w[i][p] = (kr < H && c < r ? wrow[c] : 0u) |
-                            ((kr < H && c + 1 < r ? (uint32_t)wrow[c + 1] : 0u) << 16);
-            }
-        }
-    }
-}
-
-template <int NT>
-__device__ __forceinline__ void mma_step(const Step<NT> &s, f32x4 *acc) {
-    const bf16x8 a = __builtin_bit_cast(bf16x8, s.a);
-    if (NT == 1) {
-        const u32x4 b = u32x4{lo_pair(s.w[0][0], s.w[1][0]), lo_pair(s.w[2][0], s.w[3][0]),
-                              lo_pair(s.w[4][0], s.w[5][0]), lo_pair(s.w[6][0], s.w[7][0])};
-        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, b), acc[0], 0, 0, 0);
-        return;
-    }
-#pragma unroll
-    for (int p = 0; p < Step<NT>::NP; ++p) {
-        const u32x4 blo = u32x4{lo_pair(s.w[0][p], s.w[1][p]), lo_pair(s.w[2][p], s.w[3][p]),
-                                lo_pair(s.w[4][p], s.w[5][p]), lo_pair(s.w[6][p], s.w[7][p])};
-        const u32x4 bhi = u32x4{hi_pair(s.w[0][p], s.w[1][p]), hi_pair(s.w[2][p], s.w[3][p]),
-                                hi_pair(s.w[4][p], s.w[5][p]), hi_pair(s.w[6][p], s.w[7][p])};
-        acc[2 * p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, blo),
-                                                             acc[2 * p], 0, 0, 0);
-        acc[2 * p + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bhi),
-                                                                 acc[2 * p + 1], 0, 0, 0);
-    }
-}
-
-// Steps whose loads are issued together, by tile count (bounded by registers).
-template <int NT> constexpr int batch_steps() { return NT <= 4 ? 4 : (NT == 8 ? 2 : 1); }
 
 template <int NT>
 __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
     const uint16_t *__restrict__ hidden, const uint16_t *__restrict__ W, int R, int H, int r,
     int splits, float *__restrict__ out) {
     constexpr int NC = NT * 16;
-    constexpr int D = batch_steps<NT>();
     __shared__ float red[kGateWaves][16][NC + (NT == 16 ? 0 : 1)];  // <= 64 KB
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int m = lane & 15, g = lane >> 4;
-    const int row = blockIdx.x * 16 + m;
-    const bool row_ok = row < R;
-    const uint16_t *hrow = hidden + (int64_t)(row_ok ? row : 0) * H;
-    const bool vec_h = (H % 8) == 0;
-
-    const int nsteps = (H + kStepK - 1) / kStepK;
-    const int q = blockIdx.y * kGateWaves + wave, nq = splits * kGateWaves;
-    const int s0 = (int)((int64_t)nsteps * q / nq), s1 = (int)((int64_t)nsteps * (q + 1) / nq);
-
+    int s0, s1;
+    gate_steps(H, blockIdx.y * kGateWaves + wave, splits * kGateWaves, s0, s1);
     f32x4 acc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // Full batches of D steps on the fast path; everything else (ragged H, odd r) step by step.
-    const bool fast_ok = vec_h && r == NC;
-    int s = s0;
-    if (fast_ok) {
-        for (; s + D <= s1 && (s + D) * kStepK <= H; s += D) {
-            Step<NT> st[D];
-#pragma unroll
-            for (int d = 0; d < D; ++d)
-                load_step<NT, true>(st[d], hrow, row_ok, W, H, r, (s + d) * kStepK, g, m);
-#pragma unroll
-            for (int d = 0; d < D; ++d) mma_step<NT>(st[d], acc);
-        }
-    }
-    for (; s < s1; ++s) {
-        Step<NT> st;
-        load_step<NT, false>(st, hrow, row_ok, W, H, r, s * kStepK, g, m);
-        mma_step<NT>(st, acc);
-    }
+    gate_wave<NT>(hidden, W, R, H, r, blockIdx.x * 16, s0, s1, lane, acc);
 
     // acc[t][i]: row g*4+i of the tile, column out_col(t, m). Sum the 4 waves in order.
 #pragma unroll

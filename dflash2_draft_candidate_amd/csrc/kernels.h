@@ -15,11 +15,22 @@ struct TopkPlan {
     int chunk_batches;  // batches per chunk handed to a wave
     int chunks;         // chunks per unit (at most)
 };
-TopkPlan plan_topk(int R, int V, int elem_bytes);
+// lds_reserve: dynamic LDS the pass needs besides its chunk sums (the fused gate's tiles).
+TopkPlan plan_topk(int R, int V, int elem_bytes, size_t lds_reserve = 0);
 size_t topk_workspace_bytes(const TopkPlan &plan, int R);
+// The gate product carried by the top-k pass (bf16 hidden and W_sel, r <= 128): it writes
+// fused_gate_splits(...) partial products [splits][R][r] floats to `part`.
+struct FusedGate {
+    const void *hidden;
+    const void *W_sel;
+    int H, r;
+    float *part;
+};
+// Splits of the fused gate for these sizes; 0 if the pass cannot carry the gate (r > 128).
+int fused_gate_splits(int R, int V, int logits_dtype, int H, int r);
 hipError_t launch_topk_lse(const void *logits, int logits_dtype, int R, int V, int k,
                            int32_t *cand_ids, float *unary, float *lse, void *workspace,
-                           hipStream_t stream);
+                           hipStream_t stream, const FusedGate *gate = nullptr);
 
 // ---- K2: gate GEMM ---------------------------------------------------------------------------
 // bf16 runs as `gate_splits` partial products over ranges of H, [splits][R][r] floats;
@@ -38,6 +49,14 @@ hipError_t launch_lattice(const int32_t *cand_ids, const float *unary, const flo
                           int ksplit, const void *pred_cb, const void *succ_cb, int cb_dtype,
                           const int32_t *anchor_ids, int B, int L, int V, int r, int k,
                           float *edges, hipStream_t stream);
+// The lattice with the greedy walk in the same kernel (one workgroup per sequence); for blocks
+// where lattice_walk_fits(L, k). path_idx may be null.
+bool lattice_walk_fits(int L, int k);
+hipError_t launch_lattice_walk(const int32_t *cand_ids, const float *unary, const float *gpart,
+                               int ksplit, const void *pred_cb, const void *succ_cb, int cb_dtype,
+                               const int32_t *anchor_ids, int B, int L, int V, int r, int k,
+                               float *edges, int32_t *path, int32_t *path_idx,
+                               hipStream_t stream);
 
 // ---- K4: walk --------------------------------------------------------------------------------
 hipError_t launch_walk(const float *edges, const int32_t *cand_ids, int B, int L, int k,

@@ -1,4 +1,4 @@
-// K3: the k x k transition lattice of every draft position.
+// K3 (+ K4): the k x k transition lattice of every draft position, and the greedy walk.
 //
 // edges[b][p][i][j] = unary[b][p][j] + sum_d pred_cb[prev_i][d] * succ_cb[cand_j][d] * g[b][p][d]
 // with prev_i = anchor_ids[b] at p = 0 and cand_ids[b][p-1][i] after. Source: "DFlash 2: Keep
@@ -6,180 +6,330 @@
 // S_t(a,b) = U_t(b) + <A(a) (.) H(h_t), B(b)>; "DFlash2 Lands in llama.cpp" (ramgpt.org), section
 // "What llama.cpp Actually Builds for the Selector" (successor rows of the current candidates,
 // predecessor rows of the previous ones, the hidden gate of the current position; the anchor is
-// the first predecessor).
+// the first predecessor). The walk: j_0 = argmax_j edges[b][0][0][j], j_p = argmax_j
+// edges[b][p][j_{p-1}][j], ties to the lowest j (same sources: greedy from the last verified
+// token, best successor of the chosen predecessor).
 //
-// One workgroup per position, built to keep the dependent global round trips at two:
-//   1. candidate ids, predecessor ids, unary scores and the gate row (the gate arrives as
-//      `ksplit` partial rows, summed here in split order);
-//   2. the 2k codebook rows, gathered with 16-byte loads and widened into LDS as fp32, the
-//      predecessor rows already multiplied by the gate (a chunk of the rank at a time when
-//      2 k r floats would not fit).
-// Each thread then accumulates its edges with fp32 FMA in rank order from float4 LDS reads.
-// A predecessor or candidate id outside [0, V) yields NaN edges instead of an out-of-bounds read.
+// Per position the lattice is a small product E = (P * g) S^T with P, S the gathered [k, r]
+// codebook rows: it runs on the matrix cores (v_mfma_f32_16x16x4_f32, fp32 in and out). A wave
+// owns one position and one 16-row tile of predecessors (KT = ceil(k / 16) waves per position)
+// and all KT column tiles. The rank is cut into chunks of 64: within a chunk, lane group
+// g = lane / 16 holds ranks 16g .. 16g + 15 of its rows, and MFMA step s takes rank 16g + s from
+// group g (any assignment of ranks to steps gives the same sum; this one lets every lane fetch
+// its 16 ranks with 16-byte loads). The chain per position is two dependent global round trips:
+// ids, unary and the gate partials, then the codebook rows.
+//
+// The walk rides in the same workgroup: one workgroup per sequence computes every position, each
+// wave reduces its rows to the best successor best[p][i] (wave-level argmax over a 64-bit key,
+// lowest j on ties), and the oldest wave chases j_p = best[p][j_{p-1}] with v_readlane, one pass
+// of positions at a time. Without the walk, a workgroup takes one pass of one sequence.
+//
+// Invalid ids: a row whose predecessor or candidate id lies outside [0, V) is written as NaN
+// (row 0 is read in its place). The walk then follows the stand-alone walk's rule: a NaN at
+// j = 0 makes j = 0 the choice, a NaN elsewhere never wins.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
 namespace dflash2 {
 namespace {
 
-constexpr int kLatThreads = 256;
-constexpr int kMaxEdgesPerThread = 64 * 64 / kLatThreads;  // k <= 64
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <typename CB> struct Cb;
-template <> struct Cb<float> {
-    static constexpr int kVec = 4;
-    static __device__ __forceinline__ float one(const float *p, int64_t i) { return p[i]; }
+constexpr int kLatWaves = 16;                 // waves per workgroup at most
+
+// Waves per workgroup for KT tiles: 4 x 4 tiles per wave hold too many registers for 16 waves.
+constexpr int lat_waves(int kt) { return kt == 4 ? 8 : kLatWaves; }
+constexpr int kRankChunk = 64;                // ranks per chunk: 4 lane groups x 16 steps
+constexpr int kMaxPasses = 4;                 // the walk rides along up to this many passes
+
+// 16 consecutive codebook values of one row as raw 16-byte vectors.
+template <typename CB>
+struct Seg {
+    static constexpr int EV = Elem<CB>::kPerVec;
+    static constexpr int NV = 16 / EV;  // 2 (bf16) or 4 (fp32) vectors
+    u32x4 v[NV];
 };
-template <> struct Cb<uint16_t> {
-    static constexpr int kVec = 8;
-    static __device__ __forceinline__ float one(const uint16_t *p, int64_t i) { return bf16_to_f32(p[i]); }
-};
 
-template <typename CB, bool VEC>
-__global__ __launch_bounds__(kLatThreads) void lattice_kernel(
-    const int32_t *__restrict__ cand_ids, const float *__restrict__ unary,
-    const float *__restrict__ gpart, int ksplit, const CB *__restrict__ pred,
-    const CB *__restrict__ succ, const int32_t *__restrict__ anchor, int L, int V, int r, int k,
-    int dc, float *__restrict__ edges) {
-    extern __shared__ __attribute__((aligned(16))) float lds[];
-    __shared__ int32_t prev_s[64], cand_s[64];
-    __shared__ float u_s[64];
-    __shared__ float g_s[256];
-    const int pitch = VEC ? dc + 4 : dc + 1;  // float4-aligned rows, or odd pitch for scalar reads
-    float *P = lds;                           // [k][pitch]: pred row * gate
-    float *S = lds + k * pitch;               // [k][pitch]: succ row
-
-    const int tid = threadIdx.x;
-    const int64_t row = blockIdx.x;
-    const int64_t R = gridDim.x;
-    const int b = (int)(row / L), p = (int)(row % L);
-
-    // Round trip 1: ids, unary, gate (independent of each other).
-    if (tid < k) {
-        prev_s[tid] = (p == 0) ? anchor[b] : cand_ids[(row - 1) * k + tid];
-        cand_s[tid] = cand_ids[row * k + tid];
-        u_s[tid] = unary[row * k + tid];
+// Ranks seg .. seg + 15 of `row` (zeros past nval). vec: whole 16-byte vectors in bounds.
+template <typename CB>
+__device__ __forceinline__ void load_seg(Seg<CB> &s, const CB *row, int seg, int nval, bool vec) {
+    if (vec) {
+#pragma unroll
+        for (int q = 0; q < Seg<CB>::NV; ++q)
+            s.v[q] = *reinterpret_cast<const u32x4 *>(row + seg + q * Seg<CB>::EV);
+        return;
     }
-    for (int d = tid; d < r; d += kLatThreads) {
-        // the split partials are independent loads: issue 8 at a time, then add in split order
-        float v = 0.f;
-        for (int s = 0; s < ksplit; s += 8) {
-            float part[8];
+    CB tmp[16];
 #pragma unroll
-            for (int q = 0; q < 8; ++q)  // clamped split index: unconditional loads
-                part[q] = gpart[((int64_t)min(s + q, ksplit - 1) * R + row) * r + d];
+    for (int e = 0; e < 16; ++e) tmp[e] = e < nval ? row[seg + e] : CB(0);
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                if (s + q < ksplit) v += part[q];
-        }
-        g_s[d] = v;
-    }
-    __syncthreads();
-
-    const int kk = k * k;
-    float acc[kMaxEdgesPerThread];
-#pragma unroll
-    for (int t = 0; t < kMaxEdgesPerThread; ++t) acc[t] = 0.f;
-
-    for (int d0 = 0; d0 < r; d0 += dc) {
-        const int dn = min(dc, r - d0);
-        // Round trip 2: gather 2k codebook rows (columns d0 .. d0+dn) into LDS.
-        if (VEC) {
-            constexpr int NV = Cb<CB>::kVec;
-            const int per_row = dn / NV;
-            for (int t = tid; t < 2 * k * per_row; t += kLatThreads) {
-                const int rr = t / per_row, d = (t % per_row) * NV;
-                const bool is_succ = rr >= k;
-                const int i = is_succ ? rr - k : rr;
-                const int32_t id = is_succ ? cand_s[i] : prev_s[i];
-                const bool ok = id >= 0 && id < V;
-                // branch-free: an invalid id reads row 0 and is replaced by NaN afterwards
-                const CB *src = (is_succ ? succ : pred) + (int64_t)(ok ? id : 0) * r + d0 + d;
-                float v[NV];
-                Elem<CB>::unpack(*reinterpret_cast<const u32x4 *>(src), v);
-#pragma unroll
-                for (int e = 0; e < NV; ++e) v[e] = ok ? v[e] : __builtin_nanf("");
-                float *dst = (is_succ ? S : P) + i * pitch + d;
-#pragma unroll
-                for (int e = 0; e < NV; ++e) dst[e] = is_succ ? v[e] : v[e] * g_s[d0 + d + e];
-            }
-        } else {
-            for (int t = tid; t < 2 * k * dn; t += kLatThreads) {
-                const int rr = t / dn, d = t % dn;
-                const bool is_succ = rr >= k;
-                const int i = is_succ ? rr - k : rr;
-                const int32_t id = is_succ ? cand_s[i] : prev_s[i];
-                const bool ok = id >= 0 && id < V;
-                float v = Cb<CB>::one(is_succ ? succ : pred, (int64_t)(ok ? id : 0) * r + d0 + d);
-                v = ok ? v : __builtin_nanf("");
-                (is_succ ? S : P)[i * pitch + d] = is_succ ? v : v * g_s[d0 + d];
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int t = 0; t < kMaxEdgesPerThread; ++t) {
-            const int e = tid + t * kLatThreads;
-            if (e < kk) {
-                const float *pi = P + (e / k) * pitch;
-                const float *sj = S + (e % k) * pitch;
-                float a = acc[t];
-                if (VEC) {
-                    for (int d = 0; d < dn; d += 4) {
-                        const float4 x = *reinterpret_cast<const float4 *>(pi + d);
-                        const float4 y = *reinterpret_cast<const float4 *>(sj + d);
-                        a = fmaf(x.x, y.x, a);
-                        a = fmaf(x.y, y.y, a);
-                        a = fmaf(x.z, y.z, a);
-                        a = fmaf(x.w, y.w, a);
-                    }
-                } else {
-                    for (int d = 0; d < dn; ++d) a = fmaf(pi[d], sj[d], a);
-                }
-                acc[t] = a;
-            }
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int t = 0; t < kMaxEdgesPerThread; ++t) {
-        const int e = tid + t * kLatThreads;
-        if (e < kk) edges[row * kk + e] = u_s[e % k] + acc[t];
-    }
+    for (int q = 0; q < Seg<CB>::NV; ++q) s.v[q] = *reinterpret_cast<const u32x4 *>(tmp + q * Seg<CB>::EV);
 }
 
 template <typename CB>
+__device__ __forceinline__ void widen(const Seg<CB> &s, float *x) {
+#pragma unroll
+    for (int q = 0; q < Seg<CB>::NV; ++q) Elem<CB>::unpack(s.v[q], x + q * Seg<CB>::EV);
+}
+
+// Walk key of edge value e in column j: larger key = better successor (higher edge, then lower
+// j). A NaN at j = 0 beats everything, a NaN elsewhere loses to everything.
+__device__ __forceinline__ uint64_t walk_key(float e, int j) {
+    if (e != e) return j == 0 ? ~0ull : 0ull;
+    return ((uint64_t)value_key(e) << 8) | (uint64_t)(255 - j);
+}
+
+__device__ __forceinline__ int key_col(uint64_t key) {
+    return key == ~0ull ? 0 : 255 - (int)(key & 0xFFu);
+}
+
+// Grid (B, passes): workgroup (b, c) covers positions of sequence b; with WALK it covers all of
+// them (c = 0) pass by pass, else pass c only. pp positions per pass, KT waves per position.
+// Dynamic LDS: the gate rows, [waves][rpad] floats.
+template <typename CB, int KT, bool WALK>
+__global__ __launch_bounds__(lat_waves(KT) * kWave) void lattice_kernel(
+    const int32_t *__restrict__ cand_ids, const float *__restrict__ unary,
+    const float *__restrict__ gpart, int ksplit, const CB *__restrict__ pred,
+    const CB *__restrict__ succ, const int32_t *__restrict__ anchor, int L, int V, int r, int k,
+    int pp, float *__restrict__ edges, int32_t *__restrict__ path,
+    int32_t *__restrict__ path_idx) {
+    extern __shared__ __attribute__((aligned(16))) float gsh[];
+    __shared__ int32_t best_s[WALK ? 2 : 1][kLatWaves][kWave];
+    __shared__ int32_t cand_s[WALK ? 2 : 1][kLatWaves][kWave];
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int pl = wave / KT, ti = wave % KT;
+    const int li = lane & 15, lg = lane >> 4;
+    const int b = blockIdx.x;
+    const int64_t R = (int64_t)gridDim.x * L;
+    const int rpad = (r + kRankChunk - 1) / kRankChunk * kRankChunk;
+    float *gw = gsh + (size_t)wave * rpad;
+    const bool vec = (r % Seg<CB>::EV) == 0;
+    const int passes = WALK ? (L + pp - 1) / pp : 1;
+    int prev = 0;  // walk: the chosen index at the previous position (the anchor's row is 0)
+
+    for (int pass = 0; pass < passes; ++pass) {
+        const int p0 = (WALK ? pass : (int)blockIdx.y) * pp;
+        const int np = min(pp, L - p0);
+        const int buf = WALK ? (pass & 1) : 0;
+        if (pl < np) {
+            const int p = p0 + pl;
+            const int64_t row = (int64_t)b * L + p;
+            // Round trip 1: ids, unary, gate partials (independent loads).
+            const int i = 16 * ti + li;
+            int32_t pid = 0;
+            if (i < k) pid = (p == 0) ? anchor[b] : cand_ids[(row - 1) * k + i];
+            int32_t cid[KT];
+            float u[KT];
+#pragma unroll
+            for (int tj = 0; tj < KT; ++tj) {
+                const int j = 16 * tj + li;
+                cid[tj] = j < k ? cand_ids[row * k + j] : 0;
+                u[tj] = j < k ? unary[row * k + j] : 0.f;
+            }
+            for (int d = lane; d < rpad; d += kWave) {
+                // the split partials, in split order (8 clamped loads in flight at a time)
+                float v = 0.f;
+                if (d < r) {
+                    for (int s = 0; s < ksplit; s += 8) {
+                        float part[8];
+#pragma unroll
+                        for (int q = 0; q < 8; ++q)
+                            part[q] = gpart[((int64_t)min(s + q, ksplit - 1) * R + row) * r + d];
+#pragma unroll
+                        for (int q = 0; q < 8; ++q)
+                            if (s + q < ksplit) v += part[q];
+                    }
+                }
+                gw[d] = v;
+            }
+            const bool pok = pid >= 0 && pid < V;
+            const uint32_t prow_ok = (uint32_t)__ballot(pok) & 0xFFFFu;  // bit li: row 16ti+li
+            bool cok[KT];
+#pragma unroll
+            for (int tj = 0; tj < KT; ++tj) cok[tj] = cid[tj] >= 0 && cid[tj] < V;
+            const CB *prow = pred + (int64_t)(pok ? pid : 0) * r;
+            const CB *srow[KT];
+#pragma unroll
+            for (int tj = 0; tj < KT; ++tj) srow[tj] = succ + (int64_t)(cok[tj] ? cid[tj] : 0) * r;
+            // the gate row is in LDS (written by this wave's lanes; LDS is in order per wave)
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+            // Round trip 2 (per chunk of 64 ranks): the codebook rows; then the MFMA steps.
+            f32x4 acc[KT];
+#pragma unroll
+            for (int tj = 0; tj < KT; ++tj) acc[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int c0 = 0; c0 < r; c0 += kRankChunk) {
+                const int seg = c0 + 16 * lg;
+                const int nval = max(0, min(16, r - seg));
+                const bool vseg = vec && nval == 16;
+                Seg<CB> sa, sb[KT];
+                load_seg<CB>(sa, prow, seg, nval, vseg);
+#pragma unroll
+                for (int tj = 0; tj < KT; ++tj) load_seg<CB>(sb[tj], srow[tj], seg, nval, vseg);
+                float a[16], gv[16];
+                widen<CB>(sa, a);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 t = *reinterpret_cast<const float4 *>(gw + seg + 4 * q);
+                    gv[4 * q] = t.x; gv[4 * q + 1] = t.y; gv[4 * q + 2] = t.z; gv[4 * q + 3] = t.w;
+                }
+#pragma unroll
+                for (int s = 0; s < 16; ++s) a[s] *= gv[s];
+#pragma unroll
+                for (int tj = 0; tj < KT; ++tj) {
+                    float bv[16];
+                    widen<CB>(sb[tj], bv);
+#pragma unroll
+                    for (int s = 0; s < 16; ++s)
+                        acc[tj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], bv[s], acc[tj], 0, 0, 0);
+                }
+            }
+
+            // acc[tj][t]: row 16ti + 4lg + t, column 16tj + li.
+            float *erow = edges + row * k * k;
+            uint64_t best[4] = {0ull, 0ull, 0ull, 0ull};
+#pragma unroll
+            for (int tj = 0; tj < KT; ++tj) {
+                const int j = 16 * tj + li;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int ii = 16 * ti + 4 * lg + t;
+                    float e = u[tj] + acc[tj][t];
+                    if (!((prow_ok >> (4 * lg + t)) & 1u) || !cok[tj]) e = __builtin_nanf("");
+                    if (ii < k && j < k) {
+                        erow[ii * k + j] = e;
+                        if (WALK) best[t] = kmax(best[t], walk_key(e, j));
+                    }
+                }
+            }
+            if (WALK) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+#pragma unroll
+                    for (int m = 1; m < 16; m <<= 1) best[t] = kmax(best[t], __shfl_xor(best[t], m, kWave));
+                    const int ii = 16 * ti + 4 * lg + t;
+                    if (li == 0 && ii < k) best_s[buf][pl][ii] = key_col(best[t]);
+                }
+                if (ti == 0 && lg == 0) {
+#pragma unroll
+                    for (int tj = 0; tj < KT; ++tj)
+                        if (16 * tj + li < k) cand_s[buf][pl][16 * tj + li] = cid[tj];
+                }
+            }
+        }
+        if (WALK) {
+            // Every position of the pass has its best successors in LDS. The oldest wave chases
+            // the pointers; the others go on with the next pass (the other buffer), and the pass
+            // after that starts only once this wave has reached the next barrier.
+            __syncthreads();
+            if (wave == 0) {
+                const int src = lane < k ? lane : 0;
+                int bj[kLatWaves], ct[kLatWaves];
+#pragma unroll
+                for (int q = 0; q < kLatWaves; ++q) {
+                    bj[q] = q < np ? best_s[buf][q][src] : 0;
+                    ct[q] = q < np ? cand_s[buf][q][src] : 0;
+                }
+                int out_j = 0, out_t = 0;
+#pragma unroll
+                for (int q = 0; q < kLatWaves; ++q) {
+                    if (q < np) {
+                        const int j = __builtin_amdgcn_readlane(bj[q], prev);
+                        const int tok = __builtin_amdgcn_readlane(ct[q], j);
+                        if (lane == q) {
+                            out_j = j;
+                            out_t = tok;
+                        }
+                        prev = j;
+                    }
+                }
+                if (lane < np) {
+                    path[(int64_t)b * L + p0 + lane] = out_t;
+                    if (path_idx) path_idx[(int64_t)b * L + p0 + lane] = out_j;
+                }
+            }
+        }
+    }
+}
+
+// Positions per pass for k: every wave of a workgroup busy.
+int positions_per_pass(int L, int k) {
+    const int kt = (k + 15) / 16;
+    const int KT = kt == 3 ? 4 : kt;
+    const int pp = lat_waves(KT) / KT;
+    return L < pp ? L : pp;
+}
+
+template <typename CB, int KT, bool WALK>
+void launch_kt(dim3 grid, int waves, size_t lds, hipStream_t stream, const int32_t *cand_ids,
+               const float *unary, const float *gpart, int ksplit, const CB *pred, const CB *succ,
+               const int32_t *anchor, int L, int V, int r, int k, int pp, float *edges,
+               int32_t *path, int32_t *path_idx) {
+    hipLaunchKernelGGL((lattice_kernel<CB, KT, WALK>), grid, dim3(waves * kWave), lds, stream,
+                       cand_ids, unary, gpart, ksplit, pred, succ, anchor, L, V, r, k, pp, edges,
+                       path, path_idx);
+}
+
+template <typename CB, bool WALK>
 hipError_t launch_cb(const int32_t *cand_ids, const float *unary, const float *gpart, int ksplit,
                      const void *pred_cb, const void *succ_cb, const int32_t *anchor_ids, int B,
-                     int L, int V, int r, int k, float *edges, hipStream_t stream) {
-    // Rank chunk: 2 k (dc + 4) floats of LDS stay under 48 KB.
-    int dc = 6144 / k - 4;
-    if (dc > r) dc = r;
-    const bool vec = (r % Cb<CB>::kVec) == 0;
-    if (vec) dc = dc / Cb<CB>::kVec * Cb<CB>::kVec;  // whole 16-byte vectors per chunk
-    const size_t lds = (size_t)2 * k * (dc + 4) * sizeof(float);
-    const dim3 grid((unsigned)((int64_t)B * L)), block(kLatThreads);
+                     int L, int V, int r, int k, float *edges, int32_t *path, int32_t *path_idx,
+                     hipStream_t stream) {
+    const int kt = (k + 15) / 16;
+    const int KT = kt == 3 ? 4 : kt;
+    const int pp = positions_per_pass(L, k);
+    const int waves = pp * KT;
+    const int rpad = (r + kRankChunk - 1) / kRankChunk * kRankChunk;
+    const size_t lds = (size_t)waves * rpad * sizeof(float);
+    const dim3 grid((unsigned)B, WALK ? 1u : (unsigned)((L + pp - 1) / pp));
     const CB *pred = static_cast<const CB *>(pred_cb);
     const CB *succ = static_cast<const CB *>(succ_cb);
-    if (vec)
-        hipLaunchKernelGGL((lattice_kernel<CB, true>), grid, block, lds, stream, cand_ids, unary,
-                           gpart, ksplit, pred, succ, anchor_ids, L, V, r, k, dc, edges);
+    auto go = [&](auto kernel_tag) {
+        constexpr int K = decltype(kernel_tag)::value;
+        launch_kt<CB, K, WALK>(grid, waves, lds, stream, cand_ids, unary, gpart, ksplit, pred,
+                               succ, anchor_ids, L, V, r, k, pp, edges, path, path_idx);
+    };
+    if (KT == 1)
+        go(std::integral_constant<int, 1>{});
+    else if (KT == 2)
+        go(std::integral_constant<int, 2>{});
     else
-        hipLaunchKernelGGL((lattice_kernel<CB, false>), grid, block, lds, stream, cand_ids, unary,
-                           gpart, ksplit, pred, succ, anchor_ids, L, V, r, k, dc, edges);
+        go(std::integral_constant<int, 4>{});
     return hipGetLastError();
 }
 
 }  // namespace
+
+bool lattice_walk_fits(int L, int k) {
+    const int pp = positions_per_pass(L, k);
+    return (L + pp - 1) / pp <= kMaxPasses;
+}
 
 hipError_t launch_lattice(const int32_t *cand_ids, const float *unary, const float *gpart,
                           int ksplit, const void *pred_cb, const void *succ_cb, int cb_dtype,
                           const int32_t *anchor_ids, int B, int L, int V, int r, int k,
                           float *edges, hipStream_t stream) {
     if (cb_dtype == 0)
-        return launch_cb<float>(cand_ids, unary, gpart, ksplit, pred_cb, succ_cb, anchor_ids, B, L,
-                                V, r, k, edges, stream);
-    return launch_cb<uint16_t>(cand_ids, unary, gpart, ksplit, pred_cb, succ_cb, anchor_ids, B, L,
-                               V, r, k, edges, stream);
+        return launch_cb<float, false>(cand_ids, unary, gpart, ksplit, pred_cb, succ_cb,
+                                       anchor_ids, B, L, V, r, k, edges, nullptr, nullptr, stream);
+    return launch_cb<uint16_t, false>(cand_ids, unary, gpart, ksplit, pred_cb, succ_cb, anchor_ids,
+                                      B, L, V, r, k, edges, nullptr, nullptr, stream);
+}
+
+hipError_t launch_lattice_walk(const int32_t *cand_ids, const float *unary, const float *gpart,
+                               int ksplit, const void *pred_cb, const void *succ_cb, int cb_dtype,
+                               const int32_t *anchor_ids, int B, int L, int V, int r, int k,
+                               float *edges, int32_t *path, int32_t *path_idx,
+                               hipStream_t stream) {
+    if (cb_dtype == 0)
+        return launch_cb<float, true>(cand_ids, unary, gpart, ksplit, pred_cb, succ_cb, anchor_ids,
+                                      B, L, V, r, k, edges, path, path_idx, stream);
+    return launch_cb<uint16_t, true>(cand_ids, unary, gpart, ksplit, pred_cb, succ_cb, anchor_ids,
+                                     B, L, V, r, k, edges, path, path_idx, stream);
 }
 
 }  // namespace dflash2

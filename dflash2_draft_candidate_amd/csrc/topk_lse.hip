@@ -35,7 +35,14 @@
 //     their first batches (k real elements reach it).
 //   * End. The unit's W lists are merged by a tree of bitonic merges (the top k of distinct keys
 //     is unique) and the unit's first wave writes the results. Deterministic throughout.
+//   * Fused gate (bf16 activations, r <= 128). The selector's gate product is independent of
+//     the logits, so the top-k pass can carry it: workgroup t computes split-K tile t of
+//     hidden . W_sel (the same tiles, wave ranges and summation order as the stand-alone gate
+//     kernel) on its four youngest waves before they join the stream; the last of the four to
+//     finish sums their parts through LDS and stores the tile. The work sharing lets the other
+//     twelve waves absorb the delay.
 #include "device_common.h"
+#include "gate_tile.h"
 #include "kernels.h"
 
 namespace dflash2 {
@@ -49,7 +56,7 @@ constexpr int kThreads = kWaves * kWave;
 constexpr int kMaxUnits = 8;              // units per workgroup (W = kWaves / G >= 2)
 constexpr int kTargetWorkgroups = 256;    // one per CU
 constexpr int kMinBatchesPerWave = 2;     // slices are not cut smaller than this per wave
-constexpr size_t kLdsBudget = 120 * 1024; // dynamic LDS (chunk sums) per workgroup
+constexpr size_t kLdsBudget = 120 * 1024; // dynamic LDS (chunk sums, gate tiles) per workgroup
 constexpr float kSumLimit = 0x1p100f;     // a chunk sum above this leaves the fast path
 constexpr float kSumFloor = 0x1p-60f;     // so does a unit total below this
 constexpr float kTermMargin = 1.f - 0x1p-10f;  // v_exp_f32 is far more accurate than this
@@ -97,7 +104,55 @@ struct K1Shared {
     uint32_t next_chunk[kMaxUnits];   // next chunk of the unit to hand out
     uint32_t seeded[kMaxUnits];       // waves of the unit that have published their seed
     uint32_t overflow[kMaxUnits];     // a chunk sum left the safe range
+    uint32_t gate_arrived;            // gate waves that have stored their part of the tile
 };
+
+// The gate tiles carried by the top-k pass: tile t = sp * mtiles + mt covers rows mt*16 ..
+// mt*16 + 15 over split sp of H, written to part[sp][R][r].
+struct GateJob {
+    const uint16_t *hidden;  // [R, H] bf16
+    const uint16_t *W;       // [H, r] bf16
+    float *part;             // [splits][R][r]
+    int R, H, r, mtiles, splits;
+};
+
+constexpr int kGateFirstWave = kWaves - kGateWaves;  // the youngest age class, one per SIMD
+
+template <int NT>
+constexpr size_t gate_red_floats() { return NT == 0 ? 0 : (size_t)kGateWaves * 16 * (NT * 16 + 1); }
+
+// Wave gw (0..3) of the workgroup's gate tile; the last of the four stores the tile.
+template <int NT>
+__device__ __forceinline__ void gate_tile_part(const GateJob &gj, int gw, int lane, float *red,
+                                            uint32_t *arrived) {
+    constexpr int PITCH = NT * 16 + 1;
+    const int t = blockIdx.x;
+    if (t >= gj.mtiles * gj.splits) return;
+    const int mt = t % gj.mtiles, sp = t / gj.mtiles;
+    int s0, s1;
+    gate_steps(gj.H, sp * kGateWaves + gw, gj.splits * kGateWaves, s0, s1);
+    f32x4 acc[NT];
+    gate_wave<NT>(gj.hidden, gj.W, gj.R, gj.H, gj.r, mt * 16, s0, s1, lane, acc);
+    const int m = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[(gw * 16 + g * 4 + i) * PITCH + out_col<NT>(tt, m)] = acc[tt][i];
+    uint32_t a = 0u;
+    if (lane == 0)
+        a = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (__builtin_amdgcn_readfirstlane(a) != kGateWaves - 1) return;
+    // the last of the four: every part is in LDS; add them in wave order
+    float *dst = gj.part + (int64_t)sp * gj.R * gj.r;
+    for (int e = lane; e < 16 * gj.r; e += kWave) {
+        const int rr = e / gj.r, c = e % gj.r, orow = mt * 16 + rr;
+        if (orow >= gj.R) continue;
+        float v = red[rr * PITCH + c];
+#pragma unroll
+        for (int w = 1; w < kGateWaves; ++w) v += red[(w * 16 + rr) * PITCH + c];
+        dst[(int64_t)orow * gj.r + c] = v;
+    }
+}
 
 struct WaveTopk {
     uint64_t top;          // this lane's entry of the wave's sorted list (lane = rank): the
@@ -382,14 +437,15 @@ __device__ void exact_pair(const T *logits, const UnitRange &u, int lane, float 
     }
 }
 
-// Grid: ceil(units / G) workgroups of kWaves waves; workgroup g owns units g*G .. g*G + G - 1.
-// Dynamic LDS: the chunk sums [G][nch_max][64] floats.
-template <typename T, int G>
+// Grid: ceil(units / G) workgroups of kWaves waves; workgroup g owns units g*G .. g*G + G - 1
+// (and gate tile g, if NTG > 0 and g < mtiles * splits). Dynamic LDS: the chunk sums
+// [G][nch_max][64] floats, then the gate's per-wave tiles [4][16][NTG * 16 + 1] floats.
+template <typename T, int G, int NTG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void
 topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, int CB,
                 int nch_max, int32_t *__restrict__ cand_ids, float *__restrict__ unary,
                 float *__restrict__ lse_out, uint64_t *__restrict__ part_keys,
-                float2 *__restrict__ part_lse) {
+                float2 *__restrict__ part_lse, GateJob gj) {
     constexpr int EV = Elem<T>::kPerVec;
     extern __shared__ __attribute__((aligned(16))) float chunk_sums[];
     __shared__ K1Shared sh;
@@ -421,7 +477,14 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     if (threadIdx.x == 0) sh.spilled = 0u;
     for (int i = threadIdx.x; i < kMaxUnits * kQueue; i += kThreads) (&sh.queue[0][0])[i] = 0ull;
     if (threadIdx.x < kMaxUnits) sh.seeded[threadIdx.x] = 0u;
+    if (threadIdx.x == 0) sh.gate_arrived = 0u;
     __syncthreads();  // the only barrier before the stream (every wave arrives long before data)
+
+    if constexpr (NTG > 0) {
+        if (wave >= kGateFirstWave)
+            gate_tile_part<NTG>(gj, wave - kGateFirstWave, lane,
+                                chunk_sums + (size_t)G * nch_max * kWave, &sh.gate_arrived);
+    }
 
     const int voff = lane * 16;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -671,23 +734,47 @@ __global__ __launch_bounds__(kWave) void topk_merge_kernel(
 
 size_t chunk_sum_bytes(int G, int nch_max) { return (size_t)G * nch_max * kWave * sizeof(float); }
 
+// Gate tile width (MFMA tiles of 16 columns) when the top-k pass carries the gate; 0: it cannot.
+int fused_gate_nt(int r) { return r <= 64 ? 4 : (r <= 128 ? 8 : 0); }
+
+size_t gate_red_bytes(int nt) {
+    return (nt == 4 ? gate_red_floats<4>() : nt == 8 ? gate_red_floats<8>() : 0) * sizeof(float);
+}
+
+int k1_grid(const TopkPlan &plan, int R) {
+    return (R * plan.slices + plan.groups - 1) / plan.groups;
+}
+
+template <typename T, int G>
+void launch_g(const TopkPlan &plan, int nt, dim3 grid, size_t lds, hipStream_t stream,
+              const T *logits, int V, int k, int units, int32_t *cand_ids, float *unary,
+              float *lse, uint64_t *part_keys, float2 *part_lse, const GateJob &gj) {
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(kThreads), lds, stream, logits, V, k, plan.slices,
+                           units, plan.chunk_batches, plan.chunks, cand_ids, unary, lse,
+                           part_keys, part_lse, gj);
+    };
+    if (nt == 4)
+        go(topk_lse_kernel<T, G, 4>);
+    else if (nt == 8)
+        go(topk_lse_kernel<T, G, 8>);
+    else
+        go(topk_lse_kernel<T, G, 0>);
+}
+
 template <typename T>
 hipError_t launch_k1(const TopkPlan &plan, const void *logits, int R, int V, int k,
                      int32_t *cand_ids, float *unary, float *lse, uint64_t *part_keys,
-                     float2 *part_lse, hipStream_t stream) {
+                     float2 *part_lse, int nt, const GateJob &gj, hipStream_t stream) {
     const int units = R * plan.slices;
-    const dim3 grid((unsigned)((units + plan.groups - 1) / plan.groups)), block(kThreads);
-    const size_t lds = chunk_sum_bytes(plan.groups, plan.chunks);
-    auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, grid, block, lds, stream, static_cast<const T *>(logits), V, k,
-                           plan.slices, units, plan.chunk_batches, plan.chunks, cand_ids, unary,
-                           lse, part_keys, part_lse);
-    };
+    const dim3 grid((unsigned)k1_grid(plan, R));
+    const size_t lds = chunk_sum_bytes(plan.groups, plan.chunks) + gate_red_bytes(nt);
+    const T *x = static_cast<const T *>(logits);
     switch (plan.groups) {
-    case 1: go(topk_lse_kernel<T, 1>); break;
-    case 2: go(topk_lse_kernel<T, 2>); break;
-    case 4: go(topk_lse_kernel<T, 4>); break;
-    default: go(topk_lse_kernel<T, 8>); break;
+    case 1: launch_g<T, 1>(plan, nt, grid, lds, stream, x, V, k, units, cand_ids, unary, lse, part_keys, part_lse, gj); break;
+    case 2: launch_g<T, 2>(plan, nt, grid, lds, stream, x, V, k, units, cand_ids, unary, lse, part_keys, part_lse, gj); break;
+    case 4: launch_g<T, 4>(plan, nt, grid, lds, stream, x, V, k, units, cand_ids, unary, lse, part_keys, part_lse, gj); break;
+    default: launch_g<T, 8>(plan, nt, grid, lds, stream, x, V, k, units, cand_ids, unary, lse, part_keys, part_lse, gj); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.slices == 1) return e;
@@ -698,7 +785,7 @@ hipError_t launch_k1(const TopkPlan &plan, const void *logits, int R, int V, int
 
 }  // namespace
 
-TopkPlan plan_topk(int R, int V, int elem_bytes) {
+TopkPlan plan_topk(int R, int V, int elem_bytes, size_t lds_reserve) {
     const int64_t EV = 16 / elem_bytes;
     const int64_t nvec_row = V / EV + 1;  // whole vectors of a row, rounded up
     const int64_t nb_row = (nvec_row + kStep - 1) / kStep;
@@ -724,7 +811,7 @@ TopkPlan plan_topk(int R, int V, int elem_bytes) {
     for (;;) {
         p.chunks = (int)((nb_unit + p.chunk_batches - 1) / p.chunk_batches);
         if (p.chunks < 1) p.chunks = 1;
-        if (chunk_sum_bytes(p.groups, p.chunks) <= kLdsBudget) break;
+        if (chunk_sum_bytes(p.groups, p.chunks) + lds_reserve <= kLdsBudget) break;
         p.chunk_batches *= 2;
     }
     return p;
@@ -735,17 +822,41 @@ size_t topk_workspace_bytes(const TopkPlan &p, int R) {
     return (size_t)R * p.slices * (kWave * sizeof(uint64_t) + sizeof(float2));
 }
 
+int fused_gate_splits(int R, int V, int logits_dtype, int H, int r) {
+    const int nt = fused_gate_nt(r);
+    if (nt == 0) return 0;
+    const TopkPlan plan = plan_topk(R, V, logits_dtype == 0 ? 4 : 2, gate_red_bytes(nt));
+    // one tile per workgroup; the grid holds at least R / 8 >= mtiles workgroups
+    const int mtiles = (R + 15) / 16;
+    const int most = k1_grid(plan, R) / mtiles;
+    const int s = gate_splits(R, H, 1);
+    return s < most ? s : most;
+}
+
 hipError_t launch_topk_lse(const void *logits, int logits_dtype, int R, int V, int k,
                            int32_t *cand_ids, float *unary, float *lse, void *workspace,
-                           hipStream_t stream) {
-    const TopkPlan plan = plan_topk(R, V, logits_dtype == 0 ? 4 : 2);
+                           hipStream_t stream, const FusedGate *gate) {
+    const int nt = gate ? fused_gate_nt(gate->r) : 0;
+    if (gate && nt == 0) return hipErrorInvalidValue;
+    const TopkPlan plan = plan_topk(R, V, logits_dtype == 0 ? 4 : 2, gate_red_bytes(nt));
     uint64_t *part_keys = static_cast<uint64_t *>(workspace);
     float2 *part_lse = reinterpret_cast<float2 *>(part_keys + (size_t)R * plan.slices * kWave);
+    GateJob gj{};
+    if (gate) {
+        gj.hidden = static_cast<const uint16_t *>(gate->hidden);
+        gj.W = static_cast<const uint16_t *>(gate->W_sel);
+        gj.part = gate->part;
+        gj.R = R;
+        gj.H = gate->H;
+        gj.r = gate->r;
+        gj.mtiles = (R + 15) / 16;
+        gj.splits = fused_gate_splits(R, V, logits_dtype, gate->H, gate->r);
+    }
     if (logits_dtype == 0)
         return launch_k1<float>(plan, logits, R, V, k, cand_ids, unary, lse, part_keys, part_lse,
-                                stream);
+                                nt, gj, stream);
     return launch_k1<uint16_t>(plan, logits, R, V, k, cand_ids, unary, lse, part_keys, part_lse,
-                               stream);
+                               nt, gj, stream);
 }
 
 }  // namespace dflash2

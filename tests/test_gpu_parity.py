@@ -238,6 +238,11 @@ SMALL_SELECT = [
     (4, 3, 300, 32, 8, 1, "bf16", "f32", "bf16", "normal"),
     (2, 4, 50000, 256, 256, 16, "bf16", "bf16", "bf16", "normal"),
     (3, 8, 2000, 64, 64, 32, "f32", "bf16", "bf16", "stress"),
+    # lattice + walk in one kernel over 3 and 4 passes of positions; then past 4 passes
+    (2, 40, 3000, 64, 64, 16, "bf16", "bf16", "bf16", "normal"),
+    (2, 7, 4099, 64, 40, 64, "f32", "bf16", "f32", "normal"),
+    (1, 70, 2000, 64, 64, 16, "bf16", "bf16", "bf16", "normal"),
+    (2, 9, 3001, 48, 20, 50, "bf16", "f32", "bf16", "normal"),
 ]
 
 
@@ -251,6 +256,53 @@ def test_select_shapes(lib, ref, B, L, V, H, r, k, ld, ad, cd, recipe):
     gpu = run_select(lib, x)
     want = ref.select(x.logits, x.hidden, x.W_sel, x.pred_cb, x.succ_cb, x.anchor_ids, k)
     check_select(gpu, want)
+
+
+STAGED = [("qwen3-8b-b1", None), ("serving-b64", None), ("gemma4-31b", None),
+          ("case", (3, 5, 1021, 100, 24, 7, "bf16", "bf16", "bf16", "normal")),
+          ("case", (2, 9, 3000, 520, 40, 5, "f32", "bf16", "f32", "normal"))]
+
+
+@pytest.mark.parametrize("name,shape", STAGED, ids=[n if c is None else "-".join(map(str, c))
+                                                    for n, c in STAGED])
+def test_select_matches_stages(lib, name, shape):
+    # With bf16 activations dflash2_select computes the gate inside the top-k pass. On these
+    # shapes both paths cut H into the same ranges and add in the same order, so the fused path
+    # must reproduce the stage-by-stage entry points bit for bit.
+    if shape is None:
+        s = synth.spec(name)
+    else:
+        B, L, V, H, r, k, ld, ad, cd, recipe = shape
+        s = synth.Spec("case", B, L, k, V, H, r, ld, ad, cd, recipe, 31)
+    log(f"select vs stages {s}")
+    x = synth.make_inputs(s)
+    cand, unary, edges, path = run_select(lib, x)
+    B, L, k = s.B, s.L, s.k
+    d_ids, d_unary, _ = lib.topk_lse(to_dev(x.logits).reshape(B * L, -1), k)
+    g = lib.gate(to_dev(x.hidden).reshape(B * L, -1), to_dev(x.W_sel))
+    d_edges = lib.lattice(d_ids.reshape(B, L, k), d_unary.reshape(B, L, k), g.reshape(B, L, -1),
+                          to_dev(x.pred_cb), to_dev(x.succ_cb), to_dev(x.anchor_ids))
+    d_path, _ = lib.walk(d_edges, d_ids.reshape(B, L, k))
+    torch.cuda.synchronize()
+    assert np.array_equal(cand, to_np(d_ids).reshape(B, L, k))
+    assert np.array_equal(unary.view(np.uint32), to_np(d_unary).reshape(B, L, k).view(np.uint32))
+    assert np.array_equal(edges, to_np(d_edges)), "edges differ from the staged path"
+    assert np.array_equal(path, to_np(d_path))
+
+
+def test_select_bad_anchor(lib):
+    # an anchor outside [0, V): position 0 of that sequence is NaN, and the walk takes j = 0
+    # there, as the stand-alone walk does on the same lattice
+    s = synth.Spec("case", 3, 6, 8, 5000, 64, 32, "bf16", "bf16", "bf16", "normal", 12)
+    x = synth.make_inputs(s)
+    x.anchor_ids[1] = s.V
+    cand, _, edges, path = run_select(lib, x)
+    assert np.all(np.isnan(edges[1, 0])) and np.all(np.isfinite(edges[[0, 2]]))
+    assert np.all(np.isfinite(edges[1, 1:]))
+    d_path, _ = lib.walk(to_dev(edges), to_dev(cand))
+    torch.cuda.synchronize()
+    assert np.array_equal(path, to_np(d_path))
+    assert path[1, 0] == cand[1, 0, 0]
 
 
 def test_select_deterministic(lib):
