@@ -198,7 +198,7 @@ int dflash2_select(const void *logits, int logits_dtype, const void *hidden, int
     if (e != hipSuccess) return hip_status(e);
     // Short blocks: lattice and walk in one kernel (one workgroup per sequence); long blocks
     // spread the lattice over more workgroups and walk in a second kernel.
-    if (lattice_walk_fits(L, k))
+    if (lattice_walk_fits(L, k, cb_dtype))
         return hip_status(launch_lattice_walk(cand_ids, unary, gpart, ksplit, pred_cb, succ_cb,
                                               cb_dtype, anchor_ids, B, L, V, r, k, edges, path,
                                               nullptr, s));

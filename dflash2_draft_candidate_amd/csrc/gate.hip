@@ -25,6 +25,7 @@ namespace {
 
 constexpr int kGateThreads = kGateWaves * kWave;
 constexpr int kTargetWgs = 256;
+constexpr int kMaxSplits = 8;  // the consumer adds at most this many partials, all loads at once
 
 template <int NT>
 __global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
@@ -99,6 +100,7 @@ int gate_splits(int R, int H, int act_dtype) {
     const int64_t mtiles = (R + 15) / 16;
     const int64_t nsteps = (H + kStepK - 1) / kStepK;
     int64_t s = (kTargetWgs + mtiles - 1) / mtiles;
+    if (s > kMaxSplits) s = kMaxSplits;
     const int64_t s_max = nsteps / kGateWaves;  // at least one step per wave
     if (s > s_max) s = s_max;
     return (int)(s < 1 ? 1 : s);

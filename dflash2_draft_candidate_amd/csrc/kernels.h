@@ -50,8 +50,8 @@ hipError_t launch_lattice(const int32_t *cand_ids, const float *unary, const flo
                           const int32_t *anchor_ids, int B, int L, int V, int r, int k,
                           float *edges, hipStream_t stream);
 // The lattice with the greedy walk in the same kernel (one workgroup per sequence); for blocks
-// where lattice_walk_fits(L, k). path_idx may be null.
-bool lattice_walk_fits(int L, int k);
+// where lattice_walk_fits(L, k, cb_dtype). path_idx may be null.
+bool lattice_walk_fits(int L, int k, int cb_dtype);
 hipError_t launch_lattice_walk(const int32_t *cand_ids, const float *unary, const float *gpart,
                                int ksplit, const void *pred_cb, const void *succ_cb, int cb_dtype,
                                const int32_t *anchor_ids, int B, int L, int V, int r, int k,

@@ -11,13 +11,17 @@
 // token, best successor of the chosen predecessor).
 //
 // Per position the lattice is a small product E = (P * g) S^T with P, S the gathered [k, r]
-// codebook rows: it runs on the matrix cores (v_mfma_f32_16x16x4_f32, fp32 in and out). A wave
-// owns one position and one 16-row tile of predecessors (KT = ceil(k / 16) waves per position)
-// and all KT column tiles. The rank is cut into chunks of 64: within a chunk, lane group
-// g = lane / 16 holds ranks 16g .. 16g + 15 of its rows, and MFMA step s takes rank 16g + s from
-// group g (any assignment of ranks to steps gives the same sum; this one lets every lane fetch
-// its 16 ranks with 16-byte loads). The chain per position is two dependent global round trips:
-// ids, unary and the gate partials, then the codebook rows.
+// codebook rows: it runs on the matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation). The
+// fp32 operand a = P * g is split into two bf16 values, a = hi + lo + O(2^-18 |a|) (both rounded
+// to nearest), and each is multiplied exactly (bf16 x bf16 fits fp32) by the bf16 codebook
+// value; fp32 codebooks are split the same way (hi*hi + lo*hi + hi*lo, the lo*lo term is below
+// 2^-16 |a b|). A wave owns one position and one 16-row tile of predecessors
+// (KT = ceil(k / 16) waves per position) and all KT column tiles. The rank is cut into chunks of
+// 64: within a chunk, lane group g = lane / 16 holds ranks 16g .. 16g + 15 of its rows, and MFMA
+// step t (of 2) takes ranks 16g + 8t .. 16g + 8t + 7 as its K slots 8g .. 8g + 7 (any assignment
+// of ranks to K slots gives the same sum; this one lets every lane fetch its 16 ranks with
+// 16-byte loads). The chain per position is two dependent global round trips: ids, unary and the
+// gate partials, then the codebook rows.
 //
 // The walk rides in the same workgroup: one workgroup per sequence computes every position, each
 // wave reduces its rows to the best successor best[p][i] (wave-level argmax over a 64-bit key,
@@ -36,11 +40,13 @@ namespace dflash2 {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kLatWaves = 16;                 // waves per workgroup at most
 
-// Waves per workgroup for KT tiles: 4 x 4 tiles per wave hold too many registers for 16 waves.
-constexpr int lat_waves(int kt) { return kt == 4 ? 8 : kLatWaves; }
+// Waves per workgroup for KT tiles and codebook element size cb: 4 x 4 tiles per wave (and 2 x 2
+// tiles of fp32 codebooks) hold too many registers for 16 waves.
+constexpr int lat_waves(int kt, int cb) { return kt == 4 || (kt == 2 && cb == 4) ? 8 : kLatWaves; }
 constexpr int kRankChunk = 64;                // ranks per chunk: 4 lane groups x 16 steps
 constexpr int kMaxPasses = 4;                 // the walk rides along up to this many passes
 
@@ -74,22 +80,62 @@ __device__ __forceinline__ void widen(const Seg<CB> &s, float *x) {
     for (int q = 0; q < Seg<CB>::NV; ++q) Elem<CB>::unpack(s.v[q], x + q * Seg<CB>::EV);
 }
 
-// Walk key of edge value e in column j: larger key = better successor (higher edge, then lower
-// j). A NaN at j = 0 beats everything, a NaN elsewhere loses to everything.
-__device__ __forceinline__ uint64_t walk_key(float e, int j) {
-    if (e != e) return j == 0 ? ~0ull : 0ull;
-    return ((uint64_t)value_key(e) << 8) | (uint64_t)(255 - j);
+// The gate value at offset `off` of each of the ksplit partial rows (stride apart), added in split
+// order from 0; N loads in flight at a time (clamped indices: no branch between the loads).
+template <int N>
+__device__ __forceinline__ float sum_parts(const float *gpart, int ksplit, int64_t stride,
+                                           int64_t off) {
+    float v = 0.f;
+    for (int s = 0; s < ksplit; s += N) {
+        float part[N];
+#pragma unroll
+        for (int q = 0; q < N; ++q) part[q] = gpart[min(s + q, ksplit - 1) * stride + off];
+#pragma unroll
+        for (int q = 0; q < N; ++q)
+            if (s + q < ksplit) v += part[q];
+    }
+    return v;
 }
 
-__device__ __forceinline__ int key_col(uint64_t key) {
-    return key == ~0ull ? 0 : 255 - (int)(key & 0xFFu);
+// x = hi + lo, both bf16 rounded to nearest (x - hi is exact in fp32).
+__device__ __forceinline__ void split_bf16(const float *x, bf16x8 *hi, bf16x8 *lo) {
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+        const __bf16 h = (__bf16)x[s];
+        hi[s / 8][s % 8] = h;
+        lo[s / 8][s % 8] = (__bf16)(x[s] - (float)h);
+    }
+}
+
+// Walk key of edge value e in column j < k: larger key = better successor; equal keys go to the
+// lower j. A NaN at j = 0 beats everything, a NaN elsewhere loses to everything (key 0, as for
+// the padding columns).
+__device__ __forceinline__ uint32_t walk_key(float e, int j) {
+    if (e != e) return j == 0 ? 0xFFFFFFFFu : 0u;
+    return value_key(e);
+}
+
+constexpr int kDppXor1 = 0xB1;   // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;   // quad_perm [2, 3, 0, 1]
+constexpr int kDppRor4 = 0x124;  // row_ror:4
+constexpr int kDppRor8 = 0x128;  // row_ror:8
+
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// Maximum over each row of 16 lanes, in every lane of the row.
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+    v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRor8, 0xF, 0xF, false));
+    v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRor4, 0xF, 0xF, false));
+    v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor2, 0xF, 0xF, false));
+    v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor1, 0xF, 0xF, false));
+    return v;
 }
 
 // Grid (B, passes): workgroup (b, c) covers positions of sequence b; with WALK it covers all of
 // them (c = 0) pass by pass, else pass c only. pp positions per pass, KT waves per position.
 // Dynamic LDS: the gate rows, [waves][rpad] floats.
 template <typename CB, int KT, bool WALK>
-__global__ __launch_bounds__(lat_waves(KT) * kWave) void lattice_kernel(
+__global__ __launch_bounds__(lat_waves(KT, sizeof(CB)) * kWave) void lattice_kernel(
     const int32_t *__restrict__ cand_ids, const float *__restrict__ unary,
     const float *__restrict__ gpart, int ksplit, const CB *__restrict__ pred,
     const CB *__restrict__ succ, const int32_t *__restrict__ anchor, int L, int V, int r, int k,
@@ -131,18 +177,13 @@ __global__ __launch_bounds__(lat_waves(KT) * kWave) void lattice_kernel(
                 u[tj] = j < k ? unary[row * k + j] : 0.f;
             }
             for (int d = lane; d < rpad; d += kWave) {
-                // the split partials, in split order (8 clamped loads in flight at a time)
                 float v = 0.f;
                 if (d < r) {
-                    for (int s = 0; s < ksplit; s += 8) {
-                        float part[8];
-#pragma unroll
-                        for (int q = 0; q < 8; ++q)
-                            part[q] = gpart[((int64_t)min(s + q, ksplit - 1) * R + row) * r + d];
-#pragma unroll
-                        for (int q = 0; q < 8; ++q)
-                            if (s + q < ksplit) v += part[q];
-                    }
+                    const int64_t stride = R * r, off = row * r + d;
+                    v = ksplit == 1   ? sum_parts<1>(gpart, ksplit, stride, off)
+                        : ksplit <= 2 ? sum_parts<2>(gpart, ksplit, stride, off)
+                        : ksplit <= 4 ? sum_parts<4>(gpart, ksplit, stride, off)
+                                      : sum_parts<8>(gpart, ksplit, stride, off);
                 }
                 gw[d] = v;
             }
@@ -179,41 +220,70 @@ __global__ __launch_bounds__(lat_waves(KT) * kWave) void lattice_kernel(
                 }
 #pragma unroll
                 for (int s = 0; s < 16; ++s) a[s] *= gv[s];
+                bf16x8 ahi[2], alo[2];
+                split_bf16(a, ahi, alo);
 #pragma unroll
                 for (int tj = 0; tj < KT; ++tj) {
-                    float bv[16];
-                    widen<CB>(sb[tj], bv);
+                    if constexpr (sizeof(CB) == 2) {  // bf16 codebook: exact operands
 #pragma unroll
-                    for (int s = 0; s < 16; ++s)
-                        acc[tj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], bv[s], acc[tj], 0, 0, 0);
+                        for (int t = 0; t < 2; ++t) {
+                            const bf16x8 bv = __builtin_bit_cast(bf16x8, sb[tj].v[t]);
+                            acc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[t], bv, acc[tj], 0, 0, 0);
+                            acc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[t], bv, acc[tj], 0, 0, 0);
+                        }
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) {
+                            float bv[8];
+                            Elem<CB>::unpack(sb[tj].v[2 * t], bv);
+                            Elem<CB>::unpack(sb[tj].v[2 * t + 1], bv + 4);
+                            bf16x8 bhi, blo;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                const __bf16 h = (__bf16)bv[e];
+                                bhi[e] = h;
+                                blo[e] = (__bf16)(bv[e] - (float)h);
+                            }
+                            acc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[t], bhi, acc[tj], 0, 0, 0);
+                            acc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[t], bhi, acc[tj], 0, 0, 0);
+                            acc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[t], blo, acc[tj], 0, 0, 0);
+                        }
+                    }
                 }
             }
 
             // acc[tj][t]: row 16ti + 4lg + t, column 16tj + li.
             float *erow = edges + row * k * k;
-            uint64_t best[4] = {0ull, 0ull, 0ull, 0ull};
 #pragma unroll
-            for (int tj = 0; tj < KT; ++tj) {
-                const int j = 16 * tj + li;
+            for (int t = 0; t < 4; ++t) {
+                const int ii = 16 * ti + 4 * lg + t;
+                const bool rok = (prow_ok >> (4 * lg + t)) & 1u;
+                uint32_t key[KT];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int ii = 16 * ti + 4 * lg + t;
+                for (int tj = 0; tj < KT; ++tj) {
+                    const int j = 16 * tj + li;
                     float e = u[tj] + acc[tj][t];
-                    if (!((prow_ok >> (4 * lg + t)) & 1u) || !cok[tj]) e = __builtin_nanf("");
-                    if (ii < k && j < k) {
-                        erow[ii * k + j] = e;
-                        if (WALK) best[t] = kmax(best[t], walk_key(e, j));
+                    if (!rok || !cok[tj]) e = __builtin_nanf("");
+                    key[tj] = j < k ? walk_key(e, j) : 0u;
+                    if (ii < k && j < k) erow[ii * k + j] = e;
+                }
+                if (WALK) {
+                    // best successor of row ii: the largest key of the row (16 lanes x KT
+                    // tiles), then the lowest column holding it
+                    uint32_t m = key[0];
+#pragma unroll
+                    for (int tj = 1; tj < KT; ++tj) m = umax32(m, key[tj]);
+                    m = row16_max(m);
+                    int jb = -1;
+#pragma unroll
+                    for (int tj = KT - 1; tj >= 0; --tj) {
+                        const uint32_t hits = (uint32_t)(__ballot(key[tj] == m) >> (16 * lg)) & 0xFFFFu;
+                        if (hits) jb = 16 * tj + __builtin_ctz(hits);
                     }
+                    if (li == 0 && ii < k) best_s[buf][pl][ii] = jb;
                 }
             }
             if (WALK) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-#pragma unroll
-                    for (int m = 1; m < 16; m <<= 1) best[t] = kmax(best[t], __shfl_xor(best[t], m, kWave));
-                    const int ii = 16 * ti + 4 * lg + t;
-                    if (li == 0 && ii < k) best_s[buf][pl][ii] = key_col(best[t]);
-                }
                 if (ti == 0 && lg == 0) {
 #pragma unroll
                     for (int tj = 0; tj < KT; ++tj)
@@ -228,27 +298,20 @@ __global__ __launch_bounds__(lat_waves(KT) * kWave) void lattice_kernel(
             __syncthreads();
             if (wave == 0) {
                 const int src = lane < k ? lane : 0;
-                int bj[kLatWaves], ct[kLatWaves];
+                int bj[kLatWaves];
 #pragma unroll
-                for (int q = 0; q < kLatWaves; ++q) {
-                    bj[q] = q < np ? best_s[buf][q][src] : 0;
-                    ct[q] = q < np ? cand_s[buf][q][src] : 0;
-                }
-                int out_j = 0, out_t = 0;
+                for (int q = 0; q < kLatWaves; ++q) bj[q] = q < np ? best_s[buf][q][src] : 0;
+                int out_j = 0;
 #pragma unroll
                 for (int q = 0; q < kLatWaves; ++q) {
                     if (q < np) {
                         const int j = __builtin_amdgcn_readlane(bj[q], prev);
-                        const int tok = __builtin_amdgcn_readlane(ct[q], j);
-                        if (lane == q) {
-                            out_j = j;
-                            out_t = tok;
-                        }
+                        out_j = lane == q ? j : out_j;
                         prev = j;
                     }
                 }
                 if (lane < np) {
-                    path[(int64_t)b * L + p0 + lane] = out_t;
+                    path[(int64_t)b * L + p0 + lane] = cand_s[buf][lane][out_j];
                     if (path_idx) path_idx[(int64_t)b * L + p0 + lane] = out_j;
                 }
             }
@@ -256,11 +319,11 @@ __global__ __launch_bounds__(lat_waves(KT) * kWave) void lattice_kernel(
     }
 }
 
-// Positions per pass for k: every wave of a workgroup busy.
-int positions_per_pass(int L, int k) {
+// Positions per pass for k and codebook element size cb: every wave of a workgroup busy.
+int positions_per_pass(int L, int k, int cb) {
     const int kt = (k + 15) / 16;
     const int KT = kt == 3 ? 4 : kt;
-    const int pp = lat_waves(KT) / KT;
+    const int pp = lat_waves(KT, cb) / KT;
     return L < pp ? L : pp;
 }
 
@@ -281,7 +344,7 @@ hipError_t launch_cb(const int32_t *cand_ids, const float *unary, const float *g
                      hipStream_t stream) {
     const int kt = (k + 15) / 16;
     const int KT = kt == 3 ? 4 : kt;
-    const int pp = positions_per_pass(L, k);
+    const int pp = positions_per_pass(L, k, sizeof(CB));
     const int waves = pp * KT;
     const int rpad = (r + kRankChunk - 1) / kRankChunk * kRankChunk;
     const size_t lds = (size_t)waves * rpad * sizeof(float);
@@ -304,8 +367,8 @@ hipError_t launch_cb(const int32_t *cand_ids, const float *unary, const float *g
 
 }  // namespace
 
-bool lattice_walk_fits(int L, int k) {
-    const int pp = positions_per_pass(L, k);
+bool lattice_walk_fits(int L, int k, int cb_dtype) {
+    const int pp = positions_per_pass(L, k, cb_dtype == 0 ? 4 : 2);
     return (L + pp - 1) / pp <= kMaxPasses;
 }
 

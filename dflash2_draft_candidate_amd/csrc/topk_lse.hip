@@ -38,9 +38,9 @@
 //   * Fused gate (bf16 activations, r <= 128). The selector's gate product is independent of
 //     the logits, so the top-k pass can carry it: workgroup t computes split-K tile t of
 //     hidden . W_sel (the same tiles, wave ranges and summation order as the stand-alone gate
-//     kernel) on its four youngest waves before they join the stream; the last of the four to
-//     finish sums their parts through LDS and stores the tile. The work sharing lets the other
-//     twelve waves absorb the delay.
+//     kernel) on four of its waves (one per SIMD) before they join the stream; the last of the
+//     four to finish sums their parts through LDS and stores the tile. The work sharing lets the
+//     other twelve waves absorb the delay.
 #include "device_common.h"
 #include "gate_tile.h"
 #include "kernels.h"
@@ -116,7 +116,10 @@ struct GateJob {
     int R, H, r, mtiles, splits;
 };
 
-constexpr int kGateFirstWave = kWaves - kGateWaves;  // the youngest age class, one per SIMD
+// The gate waves: four slots of one age class, one per SIMD, none of them a unit's owner (age 1;
+// age 2 when a unit has two waves). The oldest class would keep the owners busy, and the youngest
+// gets too few issue slots to finish its tile early.
+template <int G> constexpr int gate_first_wave() { return G == 8 ? 8 : 4; }
 
 template <int NT>
 constexpr size_t gate_red_floats() { return NT == 0 ? 0 : (size_t)kGateWaves * 16 * (NT * 16 + 1); }
@@ -481,8 +484,8 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     __syncthreads();  // the only barrier before the stream (every wave arrives long before data)
 
     if constexpr (NTG > 0) {
-        if (wave >= kGateFirstWave)
-            gate_tile_part<NTG>(gj, wave - kGateFirstWave, lane,
+        if (wave >= gate_first_wave<G>() && wave < gate_first_wave<G>() + kGateWaves)
+            gate_tile_part<NTG>(gj, wave - gate_first_wave<G>(), lane,
                                 chunk_sums + (size_t)G * nch_max * kWave, &sh.gate_arrived);
     }
 
