@@ -242,8 +242,8 @@ def summarize(a: list[str]):
             f"# HBM traffic of {K1_KERNEL} on {workload}\n\n"
             "Two rocprofv3 counter passes over the same command (FETCH_SIZE, then WRITE_SIZE), "
             "from the repository root on a one-GPU MI355X box:\n\n"
-            f"    rocprofv3 --pmc FETCH_SIZE ... -- {cmd}\n"
-            f"    rocprofv3 --pmc WRITE_SIZE ... -- {cmd}\n\n"
+            f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_FETCH_SIZE -o k1 -- {cmd}\n"
+            f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_WRITE_SIZE -o k1 -- {cmd}\n\n"
             f"Calibration: the runtime's copy kernel moving {copy_bytes} bytes reads "
             f"{f_cp:.1f} KiB of FETCH_SIZE and {w_cp:.1f} KiB of WRITE_SIZE per dispatch: "
             f"factors {f_factor:.4f} (fetch) and {w_factor:.4f} (write) counter bytes per byte.\n\n"
