@@ -1,7 +1,9 @@
 """Benchmark of the DFlash 2 candidate selector on one MI355X.
 
 A step is one dflash2_select call: top-k + logsumexp, gate, lattice and walk over one batch of
-synthetic logits/hidden rows already resident in HBM. Logits and hidden rows rotate through a
+synthetic logits/hidden rows already resident in HBM. Every timed loop runs its W warm-up steps
+and keeps warming (untimed) until at least WARM_SECONDS have passed: the GPU's clocks take tens
+of milliseconds of load to settle, and a selector in serving runs back to back. Logits and hidden rows rotate through a
 pool of copies larger than 1 GiB (over twice the 256 MB Infinity Cache), so every step streams
 its logits from HBM. The weights (W_sel, codebooks) are one copy, as in serving.
 
@@ -34,6 +36,7 @@ K1_SOURCE = os.path.join(ROOT, "dflash2_draft_candidate_amd", "csrc", "topk_lse.
 K1_KERNEL = "topk_lse_kernel"
 COPY_KERNEL = "copyBuffer"  # the HIP runtime's device-to-device copy kernel
 COPY_REPS = 5
+WARM_SECONDS = 0.3
 
 
 def log(*a):
@@ -102,17 +105,23 @@ class Workload:
             raise RuntimeError(f"dflash2_topk_lse failed with status {rc}")
 
 
-def time_loop(fn, steps: int, warmup: int) -> float:
-    """Mean milliseconds per call of fn(i), HIP events on the current stream."""
+def time_loop(fn, steps: int, warmup: int, warm_seconds: float = WARM_SECONDS) -> float:
+    """Mean milliseconds per call of fn(i), HIP events on the current stream, after `warmup`
+    untimed calls and as many more as fill warm_seconds."""
     import torch
-    for i in range(warmup):
+    t0 = time.time()
+    i = 0
+    while i < warmup or time.time() - t0 < warm_seconds:
         fn(i)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(steps):
-        fn(warmup + i)
+    for j in range(steps):
+        fn(i + j)
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
@@ -299,7 +308,9 @@ def main():
         wsb = d2.library().dflash2_topk_lse_workspace_bytes(
             s.R, s.V, s.k, d2.BF16 if s.logits_dtype == "bf16" else d2.F32)
         ws = torch.empty(max(16, wsb), dtype=torch.uint8, device=device)
-        ms = time_loop(lambda i: w.k1_step(i, ids, unary, lse, ws), args.steps, args.warmup)
+        # (no time-based warm-up here: under a counter collection every launch is slow)
+        ms = time_loop(lambda i: w.k1_step(i, ids, unary, lse, ws), args.steps, args.warmup,
+                       warm_seconds=0.0)
         log(f"[bench] k1-only {args.workload}: {ms * 1e3:.2f} us/launch, "
             f"{k1_bytes(s) / (ms * 1e-3) / 1e9:.1f} GB/s")
         if args.copy_mib > 0:
@@ -340,6 +351,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warm_seconds": WARM_SECONDS,
         "ms_per_step": round(main_res["e2e_us"] / 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",

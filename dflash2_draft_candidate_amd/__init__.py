@@ -51,10 +51,17 @@ _lib.dflash2_lattice.argtypes = [_vp, _vp, _vp, _vp, _vp, _ci, _vp] + [_ci] * 5 
 _lib.dflash2_lattice.restype = _ci
 _lib.dflash2_walk.argtypes = [_vp, _vp, _ci, _ci, _ci, _vp, _vp, _vp]
 _lib.dflash2_walk.restype = _ci
+_cf = ctypes.c_float
+_lib.dflash2_walk_ex.argtypes = [_vp, _vp, _ci, _ci, _ci, _cf, _vp, _cf, _vp, _vp, _vp, _vp]
+_lib.dflash2_walk_ex.restype = _ci
+_lib.dflash2_select_ex.argtypes = [_vp, _ci, _vp, _ci, _vp, _vp, _vp, _ci, _vp] + [_ci] * 6 + \
+    [_cf, _vp, _cf, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.dflash2_select_ex.restype = _ci
 
 EXPORTS = ("dflash2_version", "dflash2_status_string", "dflash2_workspace_bytes",
            "dflash2_select", "dflash2_topk_lse_workspace_bytes", "dflash2_topk_lse",
-           "dflash2_gate_workspace_bytes", "dflash2_gate", "dflash2_lattice", "dflash2_walk")
+           "dflash2_gate_workspace_bytes", "dflash2_gate", "dflash2_lattice", "dflash2_walk",
+           "dflash2_select_ex", "dflash2_walk_ex")
 
 
 class Dflash2Error(RuntimeError):
@@ -144,6 +151,47 @@ def select(logits: torch.Tensor, hidden: torch.Tensor, W_sel: torch.Tensor,
     return cand_ids, unary, edges, path
 
 
+def select_ex(logits: torch.Tensor, hidden: torch.Tensor, W_sel: torch.Tensor,
+              pred_cb: torch.Tensor, succ_cb: torch.Tensor, anchor_ids: torch.Tensor, k: int,
+              temperature: float = 0.0, uniforms: torch.Tensor | None = None, p_min: float = 0.0,
+              out: tuple | None = None, workspace: torch.Tensor | None = None):
+    """The selector with the walk's sampling (temperature > 0, uniforms [B,L] float32 in [0,1))
+    and p_min early stop. Returns (cand_ids, unary, edges, path, draft_len [B] int32)."""
+    _contig(logits, hidden, W_sel, pred_cb, succ_cb, anchor_ids)
+    B, L, V = logits.shape
+    H = hidden.shape[-1]
+    r = W_sel.shape[1]
+    if hidden.shape != (B, L, H) or W_sel.shape != (H, r) or pred_cb.shape != (V, r) \
+            or succ_cb.shape != (V, r) or anchor_ids.shape != (B,):
+        raise ValueError("inconsistent shapes")
+    if hidden.dtype != W_sel.dtype or pred_cb.dtype != succ_cb.dtype:
+        raise TypeError("hidden/W_sel and pred_cb/succ_cb must share a dtype")
+    if anchor_ids.dtype != torch.int32:
+        raise TypeError("anchor_ids must be int32")
+    if uniforms is not None:
+        _contig(uniforms)
+        if uniforms.shape != (B, L) or uniforms.dtype != torch.float32:
+            raise ValueError("uniforms must be [B, L] float32")
+    dev = logits.device
+    if out is None:
+        out = (torch.empty((B, L, k), dtype=torch.int32, device=dev),
+               torch.empty((B, L, k), dtype=torch.float32, device=dev),
+               torch.empty((B, L, k, k), dtype=torch.float32, device=dev),
+               torch.empty((B, L), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev))
+    cand_ids, unary, edges, path, draft_len = out
+    if workspace is None:
+        workspace = _workspace(workspace_bytes(B, L, V, H, r, k), dev)
+    rc = _lib.dflash2_select_ex(_ptr(logits), _dtype(logits), _ptr(hidden), _dtype(hidden),
+                                _ptr(W_sel), _ptr(pred_cb), _ptr(succ_cb), _dtype(pred_cb),
+                                _ptr(anchor_ids), B, L, V, H, r, k, float(temperature),
+                                _ptr(uniforms), float(p_min), _ptr(cand_ids), _ptr(unary),
+                                _ptr(edges), _ptr(path), _ptr(draft_len), _ptr(workspace),
+                                workspace.numel(), _stream(dev))
+    _check(rc, "dflash2_select_ex")
+    return cand_ids, unary, edges, path, draft_len
+
+
 def topk_lse(logits: torch.Tensor, k: int):
     """logits [R, V] -> (cand_ids [R,k] int32, unary [R,k] f32, lse [R] f32)."""
     _contig(logits)
@@ -209,3 +257,25 @@ def walk(edges: torch.Tensor, cand_ids: torch.Tensor):
                            _stream(dev))
     _check(rc, "dflash2_walk")
     return path, idx
+
+
+def walk_ex(edges: torch.Tensor, cand_ids: torch.Tensor, temperature: float = 0.0,
+            uniforms: torch.Tensor | None = None, p_min: float = 0.0):
+    """The walk with sampling and the p_min stop -> (path [B,L], path_idx [B,L], draft_len [B])."""
+    _contig(edges, cand_ids)
+    B, L, k = cand_ids.shape
+    if edges.shape != (B, L, k, k) or edges.dtype != torch.float32 or cand_ids.dtype != torch.int32:
+        raise ValueError("edges [B,L,k,k] float32, cand_ids [B,L,k] int32")
+    if uniforms is not None:
+        _contig(uniforms)
+        if uniforms.shape != (B, L) or uniforms.dtype != torch.float32:
+            raise ValueError("uniforms must be [B, L] float32")
+    dev = edges.device
+    path = torch.empty((B, L), dtype=torch.int32, device=dev)
+    idx = torch.empty((B, L), dtype=torch.int32, device=dev)
+    dlen = torch.empty((B,), dtype=torch.int32, device=dev)
+    rc = _lib.dflash2_walk_ex(_ptr(edges), _ptr(cand_ids), B, L, k, float(temperature),
+                              _ptr(uniforms), float(p_min), _ptr(path), _ptr(idx), _ptr(dlen),
+                              _stream(dev))
+    _check(rc, "dflash2_walk_ex")
+    return path, idx, dlen

@@ -2,6 +2,7 @@
 // Nothing here allocates device memory or synchronises; all work goes to the caller's stream.
 #include "dflash2.h"
 
+#include <float.h>
 #include <limits.h>
 
 #include "kernels.h"
@@ -141,6 +142,26 @@ int dflash2_walk(const float *edges, const int32_t *cand_ids, int B, int L, int 
                                   static_cast<hipStream_t>(stream)));
 }
 
+int dflash2_walk_ex(const float *edges, const int32_t *cand_ids, int B, int L, int k,
+                    float temperature, const float *uniforms, float p_min, int32_t *path,
+                    int32_t *path_idx, int32_t *draft_len, void *stream) {
+    if (B < 1 || L < 1 || k < 1 || k > DFLASH2_MAX_K || rows_of(B, L) > INT_MAX ||
+        !(temperature >= 0.f) || !(temperature <= FLT_MAX) || p_min != p_min)
+        return DFLASH2_ERR_INVALID_ARG;
+    if (temperature > 0.f && !uniforms) return DFLASH2_ERR_INVALID_ARG;
+    int rc = check_ptrs({edges, cand_ids, path});
+    if (rc) return rc;
+    for (const void *p : {(const void *)uniforms, (const void *)path_idx, (const void *)draft_len})
+        if (p && !aligned16(p)) return DFLASH2_ERR_ALIGNMENT;
+    WalkMode mode;
+    mode.temperature = temperature;
+    mode.uniforms = temperature > 0.f ? uniforms : nullptr;
+    mode.p_min = p_min;
+    mode.draft_len = draft_len;
+    return hip_status(launch_walk(edges, cand_ids, B, L, k, path, path_idx,
+                                  static_cast<hipStream_t>(stream), &mode));
+}
+
 size_t dflash2_workspace_bytes(int B, int L, int V, int H, int r, int k) {
     if (B < 1 || L < 1 || H < 1 || r < 1 || r > DFLASH2_MAX_R || rows_of(B, L) > INT_MAX ||
         check_rows((int)rows_of(B, L), V, k) != DFLASH2_OK)
@@ -155,11 +176,12 @@ size_t dflash2_workspace_bytes(int B, int L, int V, int H, int r, int k) {
     return most;
 }
 
-int dflash2_select(const void *logits, int logits_dtype, const void *hidden, int act_dtype,
-                   const void *W_sel, const void *pred_cb, const void *succ_cb, int cb_dtype,
-                   const int32_t *anchor_ids, int B, int L, int V, int H, int r, int k,
-                   int32_t *cand_ids, float *unary, float *edges, int32_t *path, void *workspace,
-                   size_t workspace_bytes, void *stream) {
+int dflash2_select_ex(const void *logits, int logits_dtype, const void *hidden, int act_dtype,
+                      const void *W_sel, const void *pred_cb, const void *succ_cb, int cb_dtype,
+                      const int32_t *anchor_ids, int B, int L, int V, int H, int r, int k,
+                      float temperature, const float *uniforms, float p_min, int32_t *cand_ids,
+                      float *unary, float *edges, int32_t *path, int32_t *draft_len,
+                      void *workspace, size_t workspace_bytes, void *stream) {
     if (B < 1 || L < 1 || H < 1 || r < 1 || r > DFLASH2_MAX_R || rows_of(B, L) > INT_MAX)
         return DFLASH2_ERR_INVALID_ARG;
     const int R = (int)rows_of(B, L);
@@ -170,6 +192,11 @@ int dflash2_select(const void *logits, int logits_dtype, const void *hidden, int
     if ((rc = check_ptrs({logits, hidden, W_sel, pred_cb, succ_cb, anchor_ids, cand_ids, unary,
                           edges, path})))
         return rc;
+    if (!(temperature >= 0.f) || !(temperature <= FLT_MAX) || p_min != p_min ||
+        (temperature > 0.f && !uniforms))
+        return DFLASH2_ERR_INVALID_ARG;
+    if ((uniforms && !aligned16(uniforms)) || (draft_len && !aligned16(draft_len)))
+        return DFLASH2_ERR_ALIGNMENT;
     const size_t need = dflash2_workspace_bytes(B, L, V, H, r, k);
     if (!workspace || workspace_bytes < need) return DFLASH2_ERR_WORKSPACE;
     if (!aligned16(workspace)) return DFLASH2_ERR_ALIGNMENT;
@@ -196,16 +223,31 @@ int dflash2_select(const void *logits, int logits_dtype, const void *hidden, int
         ksplit = gate_splits(R, H, act_dtype);
     }
     if (e != hipSuccess) return hip_status(e);
-    // Short blocks: lattice and walk in one kernel (one workgroup per sequence); long blocks
-    // spread the lattice over more workgroups and walk in a second kernel.
-    if (lattice_walk_fits(L, k, cb_dtype))
+    // Short blocks, greedy: lattice and walk in one kernel (one workgroup per sequence). Long
+    // blocks spread the lattice over more workgroups, and sampling runs in the walk kernel.
+    if (temperature == 0.f && lattice_walk_fits(L, k, cb_dtype))
         return hip_status(launch_lattice_walk(cand_ids, unary, gpart, ksplit, pred_cb, succ_cb,
                                               cb_dtype, anchor_ids, B, L, V, r, k, edges, path,
-                                              nullptr, s));
+                                              nullptr, p_min, draft_len, s));
     e = launch_lattice(cand_ids, unary, gpart, ksplit, pred_cb, succ_cb, cb_dtype, anchor_ids, B,
                        L, V, r, k, edges, s);
-    if (e == hipSuccess) e = launch_walk(edges, cand_ids, B, L, k, path, nullptr, s);
+    WalkMode mode;
+    mode.temperature = temperature;
+    mode.uniforms = temperature > 0.f ? uniforms : nullptr;
+    mode.p_min = p_min;
+    mode.draft_len = draft_len;
+    if (e == hipSuccess) e = launch_walk(edges, cand_ids, B, L, k, path, nullptr, s, &mode);
     return hip_status(e);
+}
+
+int dflash2_select(const void *logits, int logits_dtype, const void *hidden, int act_dtype,
+                   const void *W_sel, const void *pred_cb, const void *succ_cb, int cb_dtype,
+                   const int32_t *anchor_ids, int B, int L, int V, int H, int r, int k,
+                   int32_t *cand_ids, float *unary, float *edges, int32_t *path, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    return dflash2_select_ex(logits, logits_dtype, hidden, act_dtype, W_sel, pred_cb, succ_cb,
+                             cb_dtype, anchor_ids, B, L, V, H, r, k, 0.f, nullptr, 0.f, cand_ids,
+                             unary, edges, path, nullptr, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

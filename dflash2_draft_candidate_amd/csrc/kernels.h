@@ -55,11 +55,20 @@ bool lattice_walk_fits(int L, int k, int cb_dtype);
 hipError_t launch_lattice_walk(const int32_t *cand_ids, const float *unary, const float *gpart,
                                int ksplit, const void *pred_cb, const void *succ_cb, int cb_dtype,
                                const int32_t *anchor_ids, int B, int L, int V, int r, int k,
-                               float *edges, int32_t *path, int32_t *path_idx,
-                               hipStream_t stream);
+                               float *edges, int32_t *path, int32_t *path_idx, float p_min,
+                               int32_t *draft_len, hipStream_t stream);
 
 // ---- K4: walk --------------------------------------------------------------------------------
+// The walk's modes: temperature 0 is greedy; > 0 draws by inverse CDF from uniforms [B, L];
+// p_min > 0 writes the early-stop block length to draft_len [B] (may be null).
+struct WalkMode {
+    float temperature = 0.f;
+    const float *uniforms = nullptr;
+    float p_min = 0.f;
+    int32_t *draft_len = nullptr;
+};
 hipError_t launch_walk(const float *edges, const int32_t *cand_ids, int B, int L, int k,
-                       int32_t *path, int32_t *path_idx, hipStream_t stream);
+                       int32_t *path, int32_t *path_idx, hipStream_t stream,
+                       const WalkMode *mode = nullptr);
 
 }  // namespace dflash2

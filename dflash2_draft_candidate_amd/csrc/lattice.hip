@@ -24,9 +24,12 @@
 // gate partials, then the codebook rows.
 //
 // The walk rides in the same workgroup: one workgroup per sequence computes every position, each
-// wave reduces its rows to the best successor best[p][i] (wave-level argmax over a 64-bit key,
-// lowest j on ties), and the oldest wave chases j_p = best[p][j_{p-1}] with v_readlane, one pass
-// of positions at a time. Without the walk, a workgroup takes one pass of one sequence.
+// wave reduces its rows to the best successor best[p][i] (wave-level argmax over an
+// order-preserving key, lowest j on ties), and the oldest wave chases j_p = best[p][j_{p-1}] with
+// v_readlane, one pass of positions at a time. With p_min > 0 each row also gets its greedy
+// confidence 1 / sum_j exp(e_j - max) ("DFlash2 Lands in llama.cpp", section "p_min Means
+// Something Different Under DFlash2"), and the chase records where the drafted block ends.
+// Without the walk, a workgroup takes one pass of one sequence.
 //
 // Invalid ids: a row whose predecessor or candidate id lies outside [0, V) is written as NaN
 // (row 0 is read in its place). The walk then follows the stand-alone walk's rule: a NaN at
@@ -122,6 +125,16 @@ constexpr int kDppRor8 = 0x128;  // row_ror:8
 
 __device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
+// Sum over each row of 16 lanes, in every lane of the row (rotations: each lane adds the same
+// values in a different order; every partial is a sum of distinct lanes).
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRor8, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRor4, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppXor2, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppXor1, 0xF, 0xF, false));
+    return v;
+}
+
 // Maximum over each row of 16 lanes, in every lane of the row.
 __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
     v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRor8, 0xF, 0xF, false));
@@ -140,10 +153,12 @@ __global__ __launch_bounds__(lat_waves(KT, sizeof(CB)) * kWave) void lattice_ker
     const float *__restrict__ gpart, int ksplit, const CB *__restrict__ pred,
     const CB *__restrict__ succ, const int32_t *__restrict__ anchor, int L, int V, int r, int k,
     int pp, float *__restrict__ edges, int32_t *__restrict__ path,
-    int32_t *__restrict__ path_idx) {
+    int32_t *__restrict__ path_idx, float p_min, int32_t *__restrict__ draft_len) {
     extern __shared__ __attribute__((aligned(16))) float gsh[];
     __shared__ int32_t best_s[WALK ? 2 : 1][kLatWaves][kWave];
     __shared__ int32_t cand_s[WALK ? 2 : 1][kLatWaves][kWave];
+    __shared__ float conf_s[WALK ? 2 : 1][kLatWaves][kWave];  // p_min: confidence of each row
+    int stop = L;  // p_min: the drafted block's length (chasing wave)
 
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -259,11 +274,13 @@ __global__ __launch_bounds__(lat_waves(KT, sizeof(CB)) * kWave) void lattice_ker
                 const int ii = 16 * ti + 4 * lg + t;
                 const bool rok = (prow_ok >> (4 * lg + t)) & 1u;
                 uint32_t key[KT];
+                float ev[KT];
 #pragma unroll
                 for (int tj = 0; tj < KT; ++tj) {
                     const int j = 16 * tj + li;
                     float e = u[tj] + acc[tj][t];
                     if (!rok || !cok[tj]) e = __builtin_nanf("");
+                    ev[tj] = e;
                     key[tj] = j < k ? walk_key(e, j) : 0u;
                     if (ii < k && j < k) erow[ii * k + j] = e;
                 }
@@ -281,6 +298,16 @@ __global__ __launch_bounds__(lat_waves(KT, sizeof(CB)) * kWave) void lattice_ker
                         if (hits) jb = 16 * tj + __builtin_ctz(hits);
                     }
                     if (li == 0 && ii < k) best_s[buf][pl][ii] = jb;
+                    if (p_min > 0.f) {
+                        // confidence at the row's maximum: 1 / sum_j exp(e_j - max)
+                        const float mv = key_value(m);
+                        float z = 0.f;
+#pragma unroll
+                        for (int tj = 0; tj < KT; ++tj)
+                            z += 16 * tj + li < k ? __builtin_amdgcn_exp2f((ev[tj] - mv) * kLog2e) : 0.f;
+                        z = row16_sum(z);
+                        if (li == 0 && ii < k) conf_s[buf][pl][ii] = 1.f / z;
+                    }
                 }
             }
             if (WALK) {
@@ -299,12 +326,19 @@ __global__ __launch_bounds__(lat_waves(KT, sizeof(CB)) * kWave) void lattice_ker
             if (wave == 0) {
                 const int src = lane < k ? lane : 0;
                 int bj[kLatWaves];
+                float cf[kLatWaves];
 #pragma unroll
-                for (int q = 0; q < kLatWaves; ++q) bj[q] = q < np ? best_s[buf][q][src] : 0;
+                for (int q = 0; q < kLatWaves; ++q) {
+                    bj[q] = q < np ? best_s[buf][q][src] : 0;
+                    cf[q] = q < np && p_min > 0.f ? conf_s[buf][q][src] : 1.f;
+                }
                 int out_j = 0;
 #pragma unroll
                 for (int q = 0; q < kLatWaves; ++q) {
                     if (q < np) {
+                        const float c = __int_as_float(
+                            __builtin_amdgcn_readlane(__float_as_int(cf[q]), prev));
+                        if (stop == L && c < p_min) stop = p0 + q;
                         const int j = __builtin_amdgcn_readlane(bj[q], prev);
                         out_j = lane == q ? j : out_j;
                         prev = j;
@@ -317,6 +351,7 @@ __global__ __launch_bounds__(lat_waves(KT, sizeof(CB)) * kWave) void lattice_ker
             }
         }
     }
+    if (WALK && wave == 0 && lane == 0 && draft_len) draft_len[b] = stop;
 }
 
 // Positions per pass for k and codebook element size cb: every wave of a workgroup busy.
@@ -331,17 +366,17 @@ template <typename CB, int KT, bool WALK>
 void launch_kt(dim3 grid, int waves, size_t lds, hipStream_t stream, const int32_t *cand_ids,
                const float *unary, const float *gpart, int ksplit, const CB *pred, const CB *succ,
                const int32_t *anchor, int L, int V, int r, int k, int pp, float *edges,
-               int32_t *path, int32_t *path_idx) {
+               int32_t *path, int32_t *path_idx, float p_min, int32_t *draft_len) {
     hipLaunchKernelGGL((lattice_kernel<CB, KT, WALK>), grid, dim3(waves * kWave), lds, stream,
                        cand_ids, unary, gpart, ksplit, pred, succ, anchor, L, V, r, k, pp, edges,
-                       path, path_idx);
+                       path, path_idx, p_min, draft_len);
 }
 
 template <typename CB, bool WALK>
 hipError_t launch_cb(const int32_t *cand_ids, const float *unary, const float *gpart, int ksplit,
                      const void *pred_cb, const void *succ_cb, const int32_t *anchor_ids, int B,
                      int L, int V, int r, int k, float *edges, int32_t *path, int32_t *path_idx,
-                     hipStream_t stream) {
+                     float p_min, int32_t *draft_len, hipStream_t stream) {
     const int kt = (k + 15) / 16;
     const int KT = kt == 3 ? 4 : kt;
     const int pp = positions_per_pass(L, k, sizeof(CB));
@@ -354,7 +389,8 @@ hipError_t launch_cb(const int32_t *cand_ids, const float *unary, const float *g
     auto go = [&](auto kernel_tag) {
         constexpr int K = decltype(kernel_tag)::value;
         launch_kt<CB, K, WALK>(grid, waves, lds, stream, cand_ids, unary, gpart, ksplit, pred,
-                               succ, anchor_ids, L, V, r, k, pp, edges, path, path_idx);
+                               succ, anchor_ids, L, V, r, k, pp, edges, path, path_idx, p_min,
+                               draft_len);
     };
     if (KT == 1)
         go(std::integral_constant<int, 1>{});
@@ -378,21 +414,25 @@ hipError_t launch_lattice(const int32_t *cand_ids, const float *unary, const flo
                           float *edges, hipStream_t stream) {
     if (cb_dtype == 0)
         return launch_cb<float, false>(cand_ids, unary, gpart, ksplit, pred_cb, succ_cb,
-                                       anchor_ids, B, L, V, r, k, edges, nullptr, nullptr, stream);
+                                       anchor_ids, B, L, V, r, k, edges, nullptr, nullptr, 0.f,
+                                       nullptr, stream);
     return launch_cb<uint16_t, false>(cand_ids, unary, gpart, ksplit, pred_cb, succ_cb, anchor_ids,
-                                      B, L, V, r, k, edges, nullptr, nullptr, stream);
+                                      B, L, V, r, k, edges, nullptr, nullptr, 0.f, nullptr,
+                                      stream);
 }
 
 hipError_t launch_lattice_walk(const int32_t *cand_ids, const float *unary, const float *gpart,
                                int ksplit, const void *pred_cb, const void *succ_cb, int cb_dtype,
                                const int32_t *anchor_ids, int B, int L, int V, int r, int k,
-                               float *edges, int32_t *path, int32_t *path_idx,
-                               hipStream_t stream) {
+                               float *edges, int32_t *path, int32_t *path_idx, float p_min,
+                               int32_t *draft_len, hipStream_t stream) {
     if (cb_dtype == 0)
         return launch_cb<float, true>(cand_ids, unary, gpart, ksplit, pred_cb, succ_cb, anchor_ids,
-                                      B, L, V, r, k, edges, path, path_idx, stream);
+                                      B, L, V, r, k, edges, path, path_idx, p_min, draft_len,
+                                      stream);
     return launch_cb<uint16_t, true>(cand_ids, unary, gpart, ksplit, pred_cb, succ_cb, anchor_ids,
-                                     B, L, V, r, k, edges, path, path_idx, stream);
+                                     B, L, V, r, k, edges, path, path_idx, p_min, draft_len,
+                                     stream);
 }
 
 }  // namespace dflash2

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DFLASH2_ABI_VERSION 1
+#define DFLASH2_ABI_VERSION 2
 #define DFLASH2_MAX_K 64  /* largest top-k */
 #define DFLASH2_MAX_R 256 /* largest codebook rank r */
 #define DFLASH2_MAX_V (1 << 28) /* largest vocabulary (a row's bytes stay within 32-bit offsets) */
@@ -104,6 +104,37 @@ int dflash2_select(const void *logits, int logits_dtype, const void *hidden, int
                    size_t workspace_bytes, void *stream);
 
 /*
+ * dflash2_select_ex - dflash2_select with the walk's two further modes (dflash2_select is this
+ *   call with temperature = 0, uniforms = NULL, p_min = 0, draft_len = NULL). Same arguments,
+ *   workspace and outputs, plus:
+ *   temperature   >= 0 (finite). 0: the greedy walk. > 0: sampling, "DFlash 2: Keep Drafting
+ *                 Parallel" (inco.ai blog), section "A Lightweight Path Selector" (sampling draws
+ *                 from the same scores): at each position, given the chosen predecessor row e,
+ *                 j is drawn from softmax(e / T) by inverse CDF: with w_j = exp((e_j - max e) / T)
+ *                 and W = sum_j w_j, j is the smallest index whose running sum (in index order)
+ *                 exceeds u * W; if rounding leaves none, the last index with w_j > 0.
+ *   uniforms      [B, L] float, device, values in [0, 1): u for each position (the caller's
+ *                 random numbers; required when temperature > 0, ignored otherwise, may be NULL).
+ *   p_min         early stop, "DFlash2 Lands in llama.cpp" (ramgpt.org), section "p_min Means
+ *                 Something Different Under DFlash2": the confidence of position p is the softmax
+ *                 of its chosen row at the chosen index, exp(e_j - max e) / sum_i exp(e_i - max e)
+ *                 (not scaled by T); the drafted block ends before the first position whose
+ *                 confidence is below p_min. path is still the walk over all L positions.
+ *                 Any non-NaN value (<= 0: never stops).
+ *   draft_len     [B] int32, device, may be NULL: the drafted block length (L if nothing
+ *                 stopped it).
+ * Errors as dflash2_select; a NaN or negative/infinite temperature, a NaN p_min, or
+ * temperature > 0 without uniforms is DFLASH2_ERR_INVALID_ARG; a misaligned uniforms or draft_len
+ * is DFLASH2_ERR_ALIGNMENT. Sampling runs the lattice and the walk as two kernels.
+ */
+int dflash2_select_ex(const void *logits, int logits_dtype, const void *hidden, int act_dtype,
+                      const void *W_sel, const void *pred_cb, const void *succ_cb, int cb_dtype,
+                      const int32_t *anchor_ids, int B, int L, int V, int H, int r, int k,
+                      float temperature, const float *uniforms, float p_min, int32_t *cand_ids,
+                      float *unary, float *edges, int32_t *path, int32_t *draft_len,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * The four stages, callable one by one (same conventions; dflash2_select runs exactly these).
  *
  * dflash2_topk_lse - per row of logits [R, V]: cand_ids [R, k] and unary [R, k] as above, and
@@ -149,6 +180,14 @@ int dflash2_lattice(const int32_t *cand_ids, const float *unary, const float *g,
  */
 int dflash2_walk(const float *edges, const int32_t *cand_ids, int B, int L, int k, int32_t *path,
                  int32_t *path_idx, void *stream);
+
+/*
+ * dflash2_walk_ex - dflash2_walk with sampling and the p_min early stop, as in dflash2_select_ex
+ *   (temperature, uniforms [B, L], p_min, draft_len [B] may be NULL). No workspace.
+ */
+int dflash2_walk_ex(const float *edges, const int32_t *cand_ids, int B, int L, int k,
+                    float temperature, const float *uniforms, float p_min, int32_t *path,
+                    int32_t *path_idx, int32_t *draft_len, void *stream);
 
 #ifdef __cplusplus
 }

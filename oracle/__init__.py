@@ -74,6 +74,9 @@ class Oracle:
                                                  ci, ci, ci, ci, ci, _c_dbl_p]
         self.lib.dflash2_ref_walk.argtypes = [_c_dbl_p, _c_int_p, ci, ci, ci, _c_int_p, _c_int_p,
                                               _c_dbl_p, _c_dbl_p]
+        self.lib.dflash2_ref_walk_ex.argtypes = [_c_dbl_p, _c_int_p, ci, ci, ci, ctypes.c_double,
+                                                 _c_dbl_p, ctypes.c_double, _c_int_p, _c_int_p,
+                                                 _c_int_p, _c_dbl_p, _c_dbl_p]
         self.lib.dflash2_ref_select.argtypes = [vp, ci, vp, ci, vp, vp, vp, ci, _c_int_p, ci, ci, ci,
                                                 ci, ci, ci, _c_int_p, _c_dbl_p, _c_dbl_p, _c_int_p,
                                                 _c_dbl_p, _c_int_p, _c_dbl_p, _c_dbl_p]
@@ -153,6 +156,28 @@ class Oracle:
                                        score.ctypes.data_as(_c_dbl_p))
         self._check(rc, "walk")
         return path, idx, margin, score
+
+    def walk_ex(self, edges, cand_ids, temperature: float = 0.0, uniforms=None,
+                p_min: float = 0.0):
+        """The walk with sampling at temperature T (uniforms [B,L] in [0,1)) and the p_min early
+        stop -> path, idx, draft_len [B], conf [B,L], cdf_margin [B,L]."""
+        edges = np.ascontiguousarray(edges, dtype=np.float64)
+        cand_ids = np.ascontiguousarray(cand_ids, dtype=np.int32)
+        B, L, k = cand_ids.shape
+        u = None if uniforms is None else np.ascontiguousarray(uniforms, dtype=np.float64)
+        path = np.zeros((B, L), np.int32)
+        idx = np.zeros((B, L), np.int32)
+        dlen = np.zeros((B,), np.int32)
+        conf = np.zeros((B, L), np.float64)
+        cm = np.zeros((B, L), np.float64)
+        rc = self.lib.dflash2_ref_walk_ex(
+            edges.ctypes.data_as(_c_dbl_p), cand_ids.ctypes.data_as(_c_int_p), B, L, k,
+            float(temperature), None if u is None else u.ctypes.data_as(_c_dbl_p), float(p_min),
+            path.ctypes.data_as(_c_int_p), idx.ctypes.data_as(_c_int_p),
+            dlen.ctypes.data_as(_c_int_p), conf.ctypes.data_as(_c_dbl_p),
+            cm.ctypes.data_as(_c_dbl_p))
+        self._check(rc, "walk_ex")
+        return path, idx, dlen, conf, cm
 
     def select(self, logits, hidden, W_sel, pred_cb, succ_cb, anchor_ids, k: int) -> SelectResult:
         """The whole selector. logits [B,L,V], hidden [B,L,H], W_sel [H,r], codebooks [V,r]."""

@@ -239,6 +239,99 @@ int dflash2_ref_walk(const double *edges, const int32_t *cand_ids, int B, int L,
 }
 
 /*
+ * The walk with its two further modes, on the same lattice.
+ *
+ * Sampling at temperature T > 0 ("DFlash 2: Keep Drafting Parallel", section "A Lightweight
+ * Path Selector": sampling draws from the same scores as greedy): at position p, given the
+ * chosen predecessor, index j is drawn from softmax(edges[b][p][prev][.] / T). The draw is by
+ * inverse CDF from the caller's uniform u = uniforms[b][p] in [0, 1): with w_j = exp((e_j - m) / T)
+ * (m the row maximum) and W = sum_j w_j, j is the smallest index whose running sum
+ * w_0 + ... + w_j exceeds u * W (if rounding leaves none, the last index with w_j > 0).
+ * T = 0 is the greedy walk (lowest index among the maxima).
+ *
+ * Early stop ("DFlash2 Lands in llama.cpp", section "p_min Means Something Different Under
+ * DFlash2"): the confidence of position p is the softmax of the row's transition scores at the
+ * chosen index, conf_p = exp(e_j - m) / sum_i exp(e_i - m) (unscaled by T); the drafted block
+ * ends before the first position with conf_p < p_min: draft_len[b] is that position, or L. The
+ * walk itself still runs to the end of the block.
+ *
+ * Diagnostics (each may be NULL): path_idx [B, L]; conf [B, L]; cdf_margin [B, L], the distance
+ * of u * W from the nearest running-sum boundary, in units of W (how far the draw was from
+ * changing; +inf for greedy steps).
+ */
+int dflash2_ref_walk_ex(const double *edges, const int32_t *cand_ids, int B, int L, int k,
+                        double temperature, const double *uniforms, double p_min,
+                        int32_t *path, int32_t *path_idx, int32_t *draft_len, double *conf,
+                        double *cdf_margin)
+{
+    if (!edges || !cand_ids || !path || B < 0 || L < 1 || k < 1 || !(temperature >= 0.0) ||
+        (temperature > 0.0 && !uniforms))
+        return ORACLE_BAD_ARG;
+    double *w = malloc(sizeof(double) * (size_t)k);
+    if (!w)
+        return ORACLE_BAD_ARG;
+    for (int b = 0; b < B; ++b) {
+        int prev = 0;
+        int stop = L;
+        for (int p = 0; p < L; ++p) {
+            const size_t row = (size_t)b * L + p;
+            const double *e = edges + (row * k + prev) * k;
+            double m = e[0];
+            for (int j = 1; j < k; ++j)
+                if (e[j] > m)
+                    m = e[j];
+            int pick = 0;
+            double margin = INFINITY;
+            if (temperature == 0.0) {
+                for (int j = 1; j < k; ++j)
+                    if (e[j] > e[pick])
+                        pick = j;
+            } else {
+                double total = 0.0;
+                for (int j = 0; j < k; ++j) {
+                    w[j] = exp((e[j] - m) / temperature);
+                    total += w[j];
+                }
+                const double target = uniforms[row] * total;
+                double run = 0.0;
+                pick = -1;
+                for (int j = 0; j < k; ++j) {
+                    run += w[j];
+                    const double d = fabs(run - target) / total;
+                    if (d < margin)
+                        margin = d;
+                    if (pick < 0 && run > target)
+                        pick = j;
+                }
+                if (pick < 0) {
+                    pick = k - 1;
+                    while (pick > 0 && w[pick] == 0.0)
+                        --pick;
+                }
+            }
+            double z = 0.0;
+            for (int j = 0; j < k; ++j)
+                z += exp(e[j] - m);
+            const double c = exp(e[pick] - m) / z;
+            if (stop == L && c < p_min)
+                stop = p;
+            path[row] = cand_ids[row * k + pick];
+            if (path_idx)
+                path_idx[row] = pick;
+            if (conf)
+                conf[row] = c;
+            if (cdf_margin)
+                cdf_margin[row] = margin;
+            prev = pick;
+        }
+        if (draft_len)
+            draft_len[b] = stop;
+    }
+    free(w);
+    return ORACLE_OK;
+}
+
+/*
  * The whole selector: top-k + logsumexp, gate, lattice, walk, in that order, on host buffers.
  * Outputs: cand_ids [B,L,k], unary [B,L,k], edges [B,L,k,k], path [B,L]; optional diagnostics
  * lse [B,L], path_idx [B,L], margin [B,L], score [B] (NULL to skip).

@@ -17,7 +17,12 @@ What pins what:
   * walk: exhaustive enumeration of all k^L index paths (lexicographic greedy order), path
     score = sum of the chosen edges, margins from a sorted row, exact edge ties go to the lower
     index, and reduction to the per-position argmax of the logits (plain DFlash) for k = 1, zero
-    codebooks and a zero gate.
+    codebooks and a zero gate;
+  * sampling walk: stratified uniforms reproduce softmax(e / T) (scipy) to one stratum, a tiny
+    temperature reproduces the greedy walk, the draw follows the chosen predecessor, closed-form
+    draws and confidences on a two-candidate row;
+  * p_min stop: closed-form confidences 1 / (1 + e^-d) and the resulting block lengths, a
+    confidence exactly at p_min, k = 1.
 """
 from __future__ import annotations
 
@@ -379,11 +384,108 @@ def pin_reduces_to_argmax(o):
         assert np.array_equal(res.path, want), f"no reduction to argmax (k={k})"
 
 
+# ---------------------------------------------------- walk modes: sampling and the p_min stop
+
+def pin_sample_frequencies(o):
+    # one position, identical rows, stratified uniforms u_i = (i + 1/2) / N: the share of each
+    # index equals softmax(e / T) up to one stratum (closed form via scipy's softmax)
+    rng = np.random.default_rng(61)
+    N, k = 4000, 5
+    e = rng.normal(0, 1.5, k)
+    edges = np.broadcast_to(e, (N, 1, k, k)).copy()
+    cand = np.broadcast_to(np.arange(100, 100 + k, dtype=np.int32), (N, 1, k)).copy()
+    u = ((np.arange(N) + 0.5) / N).reshape(N, 1)
+    for T in (0.5, 1.0, 2.0):
+        _, idx, _, _, _ = o.walk_ex(edges, cand, T, u, 0.0)
+        share = np.bincount(idx[:, 0], minlength=k) / N
+        want = scipy.special.softmax(e / T)
+        assert np.all(np.abs(share - want) <= 1.0 / N + 1e-12), f"T={T}: {share} vs {want}"
+        # the stratified draws are monotone in u: indices never decrease
+        assert np.all(np.diff(idx[:, 0]) >= 0)
+
+
+def pin_sample_low_temperature_is_greedy(o):
+    # a temperature far below every gap between a row's edges concentrates the draw on the
+    # argmax: the sampled walk equals the (enumeration-pinned) greedy walk, predecessors included
+    rng = np.random.default_rng(62)
+    B, L, k = 3, 5, 6
+    edges = rng.permutation(B * L * k * k).reshape(B, L, k, k).astype(np.float64)  # gaps >= 1
+    edges[:, 0] = edges[:, 0, :1]
+    cand = rng.integers(0, 1000, (B, L, k)).astype(np.int32)
+    u = rng.uniform(0.02, 0.98, (B, L))
+    path_g, idx_g, _, _ = o.walk(edges, cand)
+    path_s, idx_s, _, _, _ = o.walk_ex(edges, cand, 0.01, u, 0.0)
+    assert np.array_equal(idx_s, idx_g) and np.array_equal(path_s, path_g)
+    path_0, idx_0, _, _, _ = o.walk_ex(edges, cand, 0.0, None, 0.0)   # T = 0: greedy itself
+    assert np.array_equal(idx_0, idx_g)
+
+
+def pin_sample_follows_predecessor(o):
+    # position 1's row i puts (almost) all mass on index i: the draw there must repeat the index
+    # drawn at position 0, whatever it was
+    k, B = 4, 64
+    e0 = np.zeros(k)
+    edges = np.zeros((B, 2, k, k))
+    edges[:, 0] = e0
+    edges[:, 1] = np.where(np.eye(k, dtype=bool), 0.0, -60.0)
+    cand = np.tile(np.arange(k, dtype=np.int32), (B, 2, 1))
+    u = np.stack([(np.arange(B) + 0.5) / B, np.full(B, 0.5)], 1)
+    _, idx, _, _, _ = o.walk_ex(edges, cand, 1.0, u, 0.0)
+    assert np.array_equal(idx[:, 1], idx[:, 0])
+    assert np.array_equal(np.bincount(idx[:, 0], minlength=k), np.full(k, B // k))
+
+
+def pin_pmin_closed_form(o):
+    # two candidates d apart: the greedy confidence is 1 / (1 + e^-d); the block ends before the
+    # first position below p_min
+    d = np.array([2.0, 1.0, 0.5, 3.0])
+    L = len(d)
+    edges = np.zeros((1, L, 2, 2))
+    edges[0, :, :, 1] = d[:, None]
+    cand = np.tile(np.array([7, 8], np.int32), (1, L, 1))
+    conf_want = 1.0 / (1.0 + np.exp(-d))
+    for p_min, want_len in [(0.0, 4), (0.6, 4), (0.7, 2), (0.8, 1), (0.9, 0), (1.0, 0)]:
+        _, idx, dlen, conf, _ = o.walk_ex(edges, cand, 0.0, None, p_min)
+        assert np.all(idx == 1)
+        assert np.allclose(conf[0], conf_want, rtol=1e-14, atol=0)
+        assert dlen[0] == want_len, f"p_min={p_min}: draft_len {dlen[0]} vs {want_len}"
+    # a confidence exactly at p_min does not stop the block (strictly below stops it)
+    edges = np.zeros((1, 3, 2, 2))
+    _, _, dlen, conf, _ = o.walk_ex(edges, np.zeros((1, 3, 2), np.int32), 0.0, None, 0.5)
+    assert np.all(conf == 0.5) and dlen[0] == 3
+    # k = 1: the confidence is 1, so only p_min > 1 ends the block at once
+    e1 = np.zeros((2, 3, 1, 1))
+    c1 = np.zeros((2, 3, 1), np.int32)
+    assert np.all(o.walk_ex(e1, c1, 0.0, None, 1.0)[2] == 3)
+    assert np.all(o.walk_ex(e1, c1, 0.0, None, 1.5)[2] == 0)
+
+
+def pin_sampled_confidence_and_margin(o):
+    # row (0, ln 3): probabilities 1/4 and 3/4. u = 0.2 draws index 0 (running sums 1/4, 1), so
+    # its confidence is 1/4 and the draw sits 0.05 of the total from the nearest boundary
+    edges = np.zeros((1, 1, 2, 2))
+    edges[0, 0, :, 1] = math.log(3.0)
+    cand = np.array([[[5, 9]]], np.int32)
+    _, idx, dlen, conf, cm = o.walk_ex(edges, cand, 1.0, np.array([[0.2]]), 0.3)
+    assert idx[0, 0] == 0 and abs(conf[0, 0] - 0.25) < 1e-15 and abs(cm[0, 0] - 0.05) < 1e-15
+    assert dlen[0] == 0   # 1/4 < 0.3
+    _, idx, _, conf, cm = o.walk_ex(edges, cand, 1.0, np.array([[0.3]]), 0.0)
+    assert idx[0, 0] == 1 and abs(conf[0, 0] - 0.75) < 1e-15 and abs(cm[0, 0] - 0.05) < 1e-15
+    # at T = 2 the probabilities are 1 / (1 + sqrt 3) and sqrt 3 / (1 + sqrt 3)
+    p0 = 1.0 / (1.0 + math.sqrt(3.0))
+    _, idx, _, conf, _ = o.walk_ex(edges, cand, 2.0, np.array([[p0 - 1e-6]]), 0.0)
+    assert idx[0, 0] == 0 and abs(conf[0, 0] - 0.25) < 1e-15   # confidence is not scaled by T
+    _, idx, _, _, _ = o.walk_ex(edges, cand, 2.0, np.array([[p0 + 1e-6]]), 0.0)
+    assert idx[0, 0] == 1
+
+
 PINS = [
     pin_topk_full_sort, pin_topk_bruteforce_rank, pin_topk_boundary_ties, pin_topk_signed_zero,
     pin_topk_shift_invariance, pin_lse_normalises, pin_lse_scipy, pin_unary_softmax,
     pin_constant_row, pin_bf16_values, pin_gate_matmul, pin_gate_onehot_rows, pin_gate_zero,
     pin_lattice_identity_gate, pin_lattice_onehot_codes, pin_lattice_zero_codebooks,
     pin_lattice_linear_in_gate, pin_lattice_anchor_rows, pin_walk_bruteforce,
-    pin_walk_score_and_margin, pin_walk_edge_tie, pin_reduces_to_argmax,
+    pin_walk_score_and_margin, pin_walk_edge_tie, pin_reduces_to_argmax, pin_sample_frequencies,
+    pin_sample_low_temperature_is_greedy, pin_sample_follows_predecessor, pin_pmin_closed_form,
+    pin_sampled_confidence_and_margin,
 ]

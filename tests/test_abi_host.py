@@ -38,6 +38,10 @@ def lib():
     L.dflash2_gate_workspace_bytes.restype = sz
     L.dflash2_lattice.argtypes = [vp, vp, vp, vp, vp, ci, vp] + [ci] * 5 + [vp, vp]
     L.dflash2_walk.argtypes = [vp, vp, ci, ci, ci, vp, vp, vp]
+    cf = ctypes.c_float
+    L.dflash2_walk_ex.argtypes = [vp, vp, ci, ci, ci, cf, vp, cf, vp, vp, vp, vp]
+    L.dflash2_select_ex.argtypes = [vp, ci, vp, ci, vp, vp, vp, ci, vp] + [ci] * 6 + \
+        [cf, vp, cf, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dflash2_status_string.argtypes = [ci]
     L.dflash2_status_string.restype = ctypes.c_char_p
     return L
@@ -52,7 +56,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     for f in ("dflash2_select", "dflash2_workspace_bytes", "dflash2_status_string",
-              "dflash2_topk_lse", "dflash2_gate", "dflash2_lattice", "dflash2_walk"):
+              "dflash2_topk_lse", "dflash2_gate", "dflash2_lattice", "dflash2_walk",
+              "dflash2_select_ex", "dflash2_walk_ex"):
         assert f in names
 
 
@@ -64,7 +69,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_binding_covers_the_abi():
     import dflash2_draft_candidate_amd as d2
     assert sorted(d2.EXPORTS) == declared_functions()
-    assert d2.version() == 1
+    assert d2.version() == 2
 
 
 def test_status_strings(lib):
@@ -119,6 +124,32 @@ def test_stage_entry_points_reject(lib):
     assert lib.dflash2_walk(P, P, 2, 3, 0, P, P, None) == EINVAL
     assert lib.dflash2_walk(P, P, 2, 3, 4, P, MIS, None) == EALIGN
     assert lib.dflash2_walk(None, P, 2, 3, 4, P, None, None) == EINVAL
+
+
+def test_mode_entry_points_reject(lib):
+    nan, inf = float("nan"), float("inf")
+    # walk_ex: sizes, temperature (negative, NaN, infinite), p_min NaN, sampling without
+    # uniforms, misaligned optional outputs
+    assert lib.dflash2_walk_ex(P, P, 2, 3, 0, 0.0, None, 0.0, P, None, None, None) == EINVAL
+    assert lib.dflash2_walk_ex(P, P, 2, 3, 4, -1.0, None, 0.0, P, None, None, None) == EINVAL
+    assert lib.dflash2_walk_ex(P, P, 2, 3, 4, nan, None, 0.0, P, None, None, None) == EINVAL
+    assert lib.dflash2_walk_ex(P, P, 2, 3, 4, inf, P, 0.0, P, None, None, None) == EINVAL
+    assert lib.dflash2_walk_ex(P, P, 2, 3, 4, 0.0, None, nan, P, None, None, None) == EINVAL
+    assert lib.dflash2_walk_ex(P, P, 2, 3, 4, 1.0, None, 0.0, P, None, None, None) == EINVAL
+    assert lib.dflash2_walk_ex(P, P, 2, 3, 4, 1.0, MIS, 0.0, P, None, None, None) == EALIGN
+    assert lib.dflash2_walk_ex(P, P, 2, 3, 4, 0.0, None, 0.5, P, None, MIS, None) == EALIGN
+    assert lib.dflash2_walk_ex(None, P, 2, 3, 4, 0.0, None, 0.0, P, None, None, None) == EINVAL
+
+    def sx(T=0.0, u=None, p_min=0.0, dlen=None, k=8, wsb=1 << 30):
+        return lib.dflash2_select_ex(P, BF16, P, BF16, P, P, P, BF16, P, 2, 4, 1000, 64, 16, k,
+                                     T, u, p_min, P, P, P, P, dlen, P, wsb, None)
+    assert sx(k=0) == EINVAL
+    assert sx(T=-0.5) == EINVAL
+    assert sx(T=nan) == EINVAL
+    assert sx(T=1.0) == EINVAL            # sampling needs uniforms
+    assert sx(p_min=nan) == EINVAL
+    assert sx(T=1.0, u=MIS) == EALIGN
+    assert sx(dlen=MIS) == EALIGN
 
 
 def test_binding_rejects_host_tensors():

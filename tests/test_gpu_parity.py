@@ -210,6 +210,77 @@ def test_walk(lib, ref, B, L, k):
         assert_ids_equal(to_np(path), rpath, "path")
 
 
+# ---------------------------------------------------------- K4 modes: sampling and p_min stop
+
+CDF_EPS = 1e-5    # a draw closer than this (in units of the row's total weight) to a boundary
+CONF_EPS = 1e-5   # a confidence closer than this to p_min may fall either way
+
+
+def check_sampled_walk(gpu_idx, gpu_dlen, edges, cand, T, u, p_min, ref):
+    """Follow the GPU's own choices: at each step the oracle (on the GPU's predecessor) fixes the
+    draw unless it lies within CDF_EPS of a CDF boundary; the GPU's draft length must be where
+    the oracle's confidences along that path first drop below p_min (up to CONF_EPS)."""
+    B, L, k = cand.shape
+    exempt = 0
+    for b in range(B):
+        prev = 0
+        stop_lo, stop_hi = L, L   # the admissible range of the block length
+        for p in range(L):
+            row = edges[b, p, prev].astype(np.float64)
+            one = np.broadcast_to(row, (1, 1, k, k)).copy()
+            _, ridx, _, rconf, rcm = ref.walk_ex(one, cand[b:b + 1, p:p + 1], T,
+                                                 None if T == 0 else u[b:b + 1, p:p + 1], p_min)
+            j = int(gpu_idx[b, p])
+            if rcm[0, 0] > CDF_EPS:
+                assert j == ridx[0, 0], f"({b},{p}): gpu drew {j}, oracle {ridx[0, 0]}"
+            else:
+                exempt += 1
+            # the confidence of the GPU's choice on this row
+            m = row.max()
+            c = math.exp(row[j] - m) / np.exp(row - m).sum()
+            if stop_hi == L and c < p_min - CONF_EPS:
+                stop_hi = p
+            if stop_lo == L and c < p_min + CONF_EPS:
+                stop_lo = p
+            prev = j
+        assert stop_lo <= gpu_dlen[b] <= stop_hi, \
+            f"seq {b}: draft_len {gpu_dlen[b]} outside [{stop_lo}, {stop_hi}]"
+    return exempt
+
+
+WALK_EX_CASES = [(3, 16, 16, 0.0, 0.5), (3, 16, 16, 1.0, 0.0), (4, 8, 32, 0.5, 0.3),
+                 (2, 40, 16, 2.0, 0.2), (2, 5, 64, 1.0, 0.05), (3, 7, 1, 1.0, 0.5),
+                 (5, 16, 16, 0.0, 0.9)]
+
+
+@pytest.mark.parametrize("B,L,k,T,p_min", WALK_EX_CASES,
+                         ids=[f"B{a}-L{b}-k{c}-T{d}-pmin{e}" for a, b, c, d, e in WALK_EX_CASES])
+def test_walk_ex(lib, ref, B, L, k, T, p_min):
+    log(f"walk_ex B={B} L={L} k={k} T={T} p_min={p_min}")
+    rng = np.random.default_rng(B * 1000 + L * 10 + k)
+    edges = rng.normal(0, 1.5, (B, L, k, k)).astype(np.float32)
+    edges[:, 0] = edges[:, 0, :1]
+    cand = rng.integers(0, 151936, (B, L, k)).astype(np.int32)
+    u = rng.random((B, L)).astype(np.float32)
+    path, idx, dlen = lib.walk_ex(to_dev(edges), to_dev(cand), T, to_dev(u) if T > 0 else None,
+                                  p_min)
+    torch.cuda.synchronize()
+    idx, path, dlen = to_np(idx), to_np(path), to_np(dlen)
+    assert np.array_equal(path, np.take_along_axis(cand, idx[..., None].astype(np.int64), 2)[..., 0])
+    exempt = check_sampled_walk(idx, dlen, edges, cand, T, u.astype(np.float64), p_min, ref)
+    log(f"  ok; near-boundary draws exempt: {exempt}")
+
+
+def test_walk_ex_greedy_matches_walk(lib):
+    rng = np.random.default_rng(5)
+    edges = rng.normal(0, 2, (4, 16, 16, 16)).astype(np.float32)
+    cand = rng.integers(0, 1000, (4, 16, 16)).astype(np.int32)
+    p0, i0 = lib.walk(to_dev(edges), to_dev(cand))
+    p1, i1, dlen = lib.walk_ex(to_dev(edges), to_dev(cand), 0.0, None, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(p0, p1) and torch.equal(i0, i1) and bool((dlen == 16).all())
+
+
 # ------------------------------------------------------------------------------- end to end
 
 def run_select(lib, x):
@@ -303,6 +374,36 @@ def test_select_bad_anchor(lib):
     torch.cuda.synchronize()
     assert np.array_equal(path, to_np(d_path))
     assert path[1, 0] == cand[1, 0, 0]
+
+
+SELECT_EX = [("serving-b64", 0.0, 0.4), ("serving-b64", 1.0, 0.2), ("stress", 0.7, 0.0),
+             ("qwen3-8b-b1", 0.0, 0.95)]
+
+
+@pytest.mark.parametrize("name,T,p_min", SELECT_EX, ids=[f"{n}-T{t}-pmin{p}" for n, t, p in SELECT_EX])
+def test_select_ex(lib, ref, name, T, p_min):
+    # the selector with the walk's modes: the lattice is select's, bit for bit; the walk on it
+    # follows the oracle's draws and confidences; the fused greedy walk agrees with the
+    # stand-alone walk kernel on the same lattice
+    x = synth.make_inputs(name)
+    s = x.spec
+    rng = np.random.default_rng(17)
+    u = rng.random((s.B, s.L)).astype(np.float32)
+    args = (to_dev(x.logits), to_dev(x.hidden), to_dev(x.W_sel), to_dev(x.pred_cb),
+            to_dev(x.succ_cb), to_dev(x.anchor_ids), s.k)
+    cand, unary, edges, path, dlen = lib.select_ex(*args, T, to_dev(u) if T > 0 else None, p_min)
+    c0, u0, e0, p0 = lib.select(*args)
+    wp, wi, wd = lib.walk_ex(edges, cand, T, to_dev(u) if T > 0 else None, p_min)
+    torch.cuda.synchronize()
+    assert torch.equal(cand, c0) and torch.equal(unary, u0) and torch.equal(edges, e0)
+    if T == 0:
+        assert torch.equal(path, p0)
+    assert torch.equal(path, wp)
+    e_np, c_np = to_np(edges), to_np(cand)
+    idx = to_np(wi)
+    check_sampled_walk(idx, to_np(dlen), e_np, c_np, T, u.astype(np.float64), p_min, ref)
+    check_sampled_walk(idx, to_np(wd), e_np, c_np, T, u.astype(np.float64), p_min, ref)
+    log(f"select_ex {name} T={T} p_min={p_min}: draft_len mean {to_np(dlen).mean():.2f}")
 
 
 def test_select_deterministic(lib):

@@ -36,6 +36,13 @@ MUTANTS = {
     "walk_ignores_predecessor": [("edges + (row * k + prev) * k", "edges + (row * k + 0) * k")],
     "walk_margin_sign": [("e[best] - second", "second - e[best]")],
     "walk_score_wrong_edge": [("total += e[best];", "total += e[0];")],
+    "sample_temperature_inverted": [("exp((e[j] - m) / temperature)", "exp((e[j] - m) * temperature)")],
+    "sample_drops_max_shift_sign": [("exp((e[j] - m) / temperature)", "exp((m - e[j]) / temperature)")],
+    "sample_ignores_predecessor": [("edges + (row * k + prev) * k;\n            double m", "edges + (row * k + 0) * k;\n            double m")],
+    "sample_uniform_complement": [("uniforms[row] * total", "(1.0 - uniforms[row]) * total")],
+    "pmin_confidence_scaled": [("z += exp(e[j] - m);", "z += exp((e[j] - m) / (temperature > 0 ? temperature : 1));")],
+    "pmin_stops_at_equality": [("c < p_min", "c <= p_min")],
+    "pmin_length_off_by_one": [("stop = p;", "stop = p + 1;")],
 }
 
 
