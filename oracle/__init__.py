@@ -77,6 +77,7 @@ class Oracle:
         self.lib.dflash2_ref_walk_ex.argtypes = [_c_dbl_p, _c_int_p, ci, ci, ci, ctypes.c_double,
                                                  _c_dbl_p, ctypes.c_double, _c_int_p, _c_int_p,
                                                  _c_int_p, _c_dbl_p, _c_dbl_p]
+        self.lib.dflash2_ref_dynconv.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, _c_dbl_p]
         self.lib.dflash2_ref_select.argtypes = [vp, ci, vp, ci, vp, vp, vp, ci, _c_int_p, ci, ci, ci,
                                                 ci, ci, ci, _c_int_p, _c_dbl_p, _c_dbl_p, _c_int_p,
                                                 _c_dbl_p, _c_int_p, _c_dbl_p, _c_dbl_p]
@@ -178,6 +179,24 @@ class Oracle:
             cm.ctypes.data_as(_c_dbl_p))
         self._check(rc, "walk_ex")
         return path, idx, dlen, conf, cm
+
+    def dynconv(self, x, base, dyn, group: int):
+        """x [nb,T,C], base [K,C], dyn [nb,T,K,C/group] (one stored dtype) -> y [nb,T,C] float64."""
+        x = np.ascontiguousarray(x)
+        base = np.ascontiguousarray(base)
+        dyn = np.ascontiguousarray(dyn)
+        nb, T, C = x.shape
+        K = base.shape[0]
+        dt = dtype_code(x)
+        if dtype_code(base) != dt or dtype_code(dyn) != dt:
+            raise ValueError("x, base and dyn must share a stored dtype")
+        if base.shape != (K, C) or dyn.shape != (nb, T, K, C // group):
+            raise ValueError("inconsistent shapes")
+        y = np.zeros((nb, T, C), np.float64)
+        rc = self.lib.dflash2_ref_dynconv(_ptr(x), _ptr(base), _ptr(dyn), dt, nb, T, C, K, group,
+                                          y.ctypes.data_as(_c_dbl_p))
+        self._check(rc, "dynconv")
+        return y
 
     def select(self, logits, hidden, W_sel, pred_cb, succ_cb, anchor_ids, k: int) -> SelectResult:
         """The whole selector. logits [B,L,V], hidden [B,L,H], W_sel [H,r], codebooks [V,r]."""

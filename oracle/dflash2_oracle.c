@@ -332,6 +332,46 @@ int dflash2_ref_walk_ex(const double *edges, const int32_t *cand_ids, int B, int
 }
 
 /*
+ * Grouped dynamic depthwise convolution of the draft blocks ("DFlash 2: Keep Drafting Parallel",
+ * section "A Lightweight Local Convolution": Conv_k(x)_t = k_{t,0} (.) x_t + k_{t,1} (.) x_{t-1},
+ * each coefficient a learned base kernel plus a correction computed from the hidden state, one
+ * correction per 16 channels, the first position reading the last verified token; "DFlash2
+ * Lands in llama.cpp", section "Dynamic Local Convolution": the sum over taps of (static
+ * weight(tap, channel) + dynamic weight(position, tap, group(channel))) * input(position - tap,
+ * channel), block-local with zero padding, the same dynamic weights on both sides of a sublayer
+ * with a base kernel per side).
+ *
+ * x [nb, T, C] (block b, row t, channel c; row 0 of a block is the last verified token),
+ * base [K, C] (one side's static kernel), dyn [nb, T, K, C / G] (the dynamic corrections of each
+ * output row and tap, one per group of G channels), all in `dtype`; out y [nb, T, C] doubles:
+ *   y[b][t][c] = sum_{tap < K} (base[tap][c] + dyn[b][t][tap][c / G]) * x[b][t - tap][c],
+ * with x[b][t'][c] = 0 for t' < 0 (nothing crosses a block boundary).
+ */
+int dflash2_ref_dynconv(const void *x, const void *base, const void *dyn, int dtype, int nb, int T,
+                        int C, int K, int G, double *y)
+{
+    if (!x || !base || !dyn || !y || !dtype_ok(dtype) || nb < 0 || T < 1 || C < 1 || K < 1 ||
+        G < 1 || C % G != 0)
+        return ORACLE_BAD_ARG;
+    const int ng = C / G;
+    for (int b = 0; b < nb; ++b)
+        for (int t = 0; t < T; ++t)
+            for (int c = 0; c < C; ++c) {
+                double acc = 0.0;
+                for (int tap = 0; tap < K; ++tap) {
+                    if (t - tap < 0)
+                        continue;  /* zero padding at the block start */
+                    const double w =
+                        oracle_value(base, dtype, (size_t)tap * C + c) +
+                        oracle_value(dyn, dtype, (((size_t)b * T + t) * K + tap) * ng + c / G);
+                    acc += w * oracle_value(x, dtype, ((size_t)b * T + (t - tap)) * C + c);
+                }
+                y[((size_t)b * T + t) * C + c] = acc;
+            }
+    return ORACLE_OK;
+}
+
+/*
  * The whole selector: top-k + logsumexp, gate, lattice, walk, in that order, on host buffers.
  * Outputs: cand_ids [B,L,k], unary [B,L,k], edges [B,L,k,k], path [B,L]; optional diagnostics
  * lse [B,L], path_idx [B,L], margin [B,L], score [B] (NULL to skip).

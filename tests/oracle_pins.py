@@ -22,7 +22,9 @@ What pins what:
     temperature reproduces the greedy walk, the draw follows the chosen predecessor, closed-form
     draws and confidences on a two-candidate row;
   * p_min stop: closed-form confidences 1 / (1 + e^-d) and the resulting block lengths, a
-    confidence exactly at p_min, k = 1.
+    confidence exactly at p_min, k = 1;
+  * dynamic convolution: with a zero dynamic part, numpy's convolve per channel; the impulse
+    response (taps, the coefficient of the output row); block locality; the group broadcast.
 """
 from __future__ import annotations
 
@@ -479,6 +481,74 @@ def pin_sampled_confidence_and_margin(o):
     assert idx[0, 0] == 1
 
 
+# ------------------------------------------------------ grouped dynamic depthwise convolution
+
+def _conv_inputs(rng, nb, T, C, K, G, dtype=F32):
+    x = rng.normal(0, 1, (nb, T, C)).astype(np.float32)
+    base = rng.normal(0, 0.5, (K, C)).astype(np.float32)
+    dyn = rng.normal(0, 0.2, (nb, T, K, C // G)).astype(np.float32)
+    if dtype == BF16:
+        cut = lambda a: (a.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+        return bf16_bits(cut(x)), bf16_bits(cut(base)), bf16_bits(cut(dyn))
+    return x, base, dyn
+
+
+def pin_conv_static_is_numpy_convolve(o):
+    # with the dynamic part zero, every channel of every block is a causal FIR filter with the
+    # channel's static taps: numpy's full convolution, truncated to the block
+    rng = np.random.default_rng(71)
+    for nb, T, C, K, G, dt in [(3, 9, 32, 2, 16, F32), (2, 17, 48, 3, 16, BF16), (1, 5, 8, 4, 4, F32)]:
+        x, base, dyn = _conv_inputs(rng, nb, T, C, K, G, dt)
+        dyn = np.zeros_like(dyn)
+        y = o.dynconv(x, base, dyn, G)
+        xw, bw = widen(x), widen(base)
+        for b in range(nb):
+            for c in range(C):
+                want = np.convolve(xw[b, :, c], bw[:, c])[:T]
+                assert np.allclose(y[b, :, c], want, rtol=1e-13, atol=1e-13)
+
+
+def pin_conv_impulse(o):
+    # a single 1 at (b, t0, c0): tap j carries it to row t0 + j of channel c0 only, with the
+    # coefficient of that output row: base[j][c0] + dyn[b][t0 + j][j][c0 / G]
+    rng = np.random.default_rng(72)
+    nb, T, C, K, G = 2, 8, 32, 3, 16
+    _, base, dyn = _conv_inputs(rng, nb, T, C, K, G)
+    b, t0, c0 = 1, 4, 21
+    x = np.zeros((nb, T, C), np.float32)
+    x[b, t0, c0] = 1.0
+    y = o.dynconv(x, base, dyn, G)
+    want = np.zeros((nb, T, C))
+    for j in range(K):
+        if t0 + j < T:
+            want[b, t0 + j, c0] = float(base[j, c0]) + float(dyn[b, t0 + j, j, c0 // G])
+    assert np.allclose(y, want, rtol=1e-15, atol=0), "impulse response"
+
+
+def pin_conv_block_local_and_grouped(o):
+    rng = np.random.default_rng(73)
+    nb, T, C, K, G = 3, 6, 64, 2, 16
+    x, base, dyn = _conv_inputs(rng, nb, T, C, K, G)
+    y = o.dynconv(x, base, dyn, G)
+    # changing one block's inputs changes no other block (zero padding, not the previous block)
+    x2 = x.copy()
+    x2[1] += 1.0
+    y2 = o.dynconv(x2, base, dyn, G)
+    assert np.array_equal(y2[[0, 2]], y[[0, 2]]) and not np.allclose(y2[1], y[1])
+    # row 0 of a block sees only tap 0
+    assert np.allclose(y[:, 0], (base[0] + np.repeat(dyn[:, 0, 0], G, axis=1)) * x[:, 0],
+                       rtol=1e-6, atol=1e-7)
+    # a correction of group g moves exactly the G channels of that group, by x of that tap
+    d2 = dyn.copy()
+    d2[2, 3, 1, 2] += 0.5
+    y3 = o.dynconv(x, base, d2, G)
+    diff = y3 - y
+    want = np.zeros_like(diff)
+    delta = float(d2[2, 3, 1, 2]) - float(dyn[2, 3, 1, 2])   # the stored (fp32) change
+    want[2, 3, 2 * G:3 * G] = delta * x[2, 2, 2 * G:3 * G].astype(np.float64)
+    assert np.allclose(diff, want, rtol=1e-9, atol=1e-12), "group broadcast"
+
+
 PINS = [
     pin_topk_full_sort, pin_topk_bruteforce_rank, pin_topk_boundary_ties, pin_topk_signed_zero,
     pin_topk_shift_invariance, pin_lse_normalises, pin_lse_scipy, pin_unary_softmax,
@@ -487,5 +557,6 @@ PINS = [
     pin_lattice_linear_in_gate, pin_lattice_anchor_rows, pin_walk_bruteforce,
     pin_walk_score_and_margin, pin_walk_edge_tie, pin_reduces_to_argmax, pin_sample_frequencies,
     pin_sample_low_temperature_is_greedy, pin_sample_follows_predecessor, pin_pmin_closed_form,
-    pin_sampled_confidence_and_margin,
+    pin_sampled_confidence_and_margin, pin_conv_static_is_numpy_convolve, pin_conv_impulse,
+    pin_conv_block_local_and_grouped,
 ]

@@ -43,6 +43,11 @@ MUTANTS = {
     "pmin_confidence_scaled": [("z += exp(e[j] - m);", "z += exp((e[j] - m) / (temperature > 0 ? temperature : 1));")],
     "pmin_stops_at_equality": [("c < p_min", "c <= p_min")],
     "pmin_length_off_by_one": [("stop = p;", "stop = p + 1;")],
+    "conv_tap_reads_ahead": [("((size_t)b * T + (t - tap)) * C + c)", "((size_t)b * T + (t + tap < T ? t + tap : t)) * C + c)")],
+    "conv_dyn_at_source_row": [("(((size_t)b * T + t) * K + tap) * ng + c / G)", "(((size_t)b * T + (t - tap)) * K + tap) * ng + c / G)")],
+    "conv_group_index_modulo": [("* ng + c / G)", "* ng + c % ng)")],
+    "conv_crosses_blocks": [("if (t - tap < 0)\n                        continue;", "if (b == 0 && t - tap < 0)\n                        continue;")],
+    "conv_drops_base": [("oracle_value(base, dtype, (size_t)tap * C + c) +", "0.0 +")],
 }
 
 
