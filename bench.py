@@ -15,6 +15,8 @@ Prints one JSON line:
                comes from committed rocprofv3 counter readings when they match the current kernel
   cpu_baseline the fp64 C oracle (single-threaded) on the host, on the same workload
   per_config   end-to-end latency and K1 bandwidth of every workload
+  extras       the default workload with the walk's sampling and p_min modes, and the grouped
+               dynamic depthwise convolution at the serving block shape
 """
 from __future__ import annotations
 
@@ -148,6 +150,58 @@ def measure(name: str, device: str, steps: int, warmup: int) -> dict:
            "k1_gbs": round(gbs, 1), "k1_frac": round(gbs / PEAK_HBM_GBS, 4)}
     res["_workload"] = w
     return res
+
+
+def measure_modes(w, steps: int, warmup: int) -> dict:
+    """The selector with the walk's further modes on a workload's inputs: sampling at T = 1
+    (staged lattice + walk kernels) and the greedy p_min stop (fused)."""
+    import torch
+    import dflash2_draft_candidate_amd as d2
+    s = w.s
+    dev = w.W.device
+    u = torch.rand((s.B, s.L), generator=torch.Generator().manual_seed(7)).to(dev)
+    out = tuple(torch.empty_like(t) for t in w.out) + (torch.empty((s.B,), dtype=torch.int32,
+                                                                   device=dev),)
+    res = {}
+    for name, T, p_min in (("sample_T1", 1.0, 0.0), ("greedy_pmin0.3", 0.0, 0.3)):
+        def step(i, T=T, p_min=p_min):
+            j = i % len(w.logits)
+            d2.select_ex(w.logits[j], w.hidden[j], w.W, w.pred, w.succ, w.anchor, s.k, T,
+                         u if T > 0 else None, p_min, out=out, workspace=w.ws)
+        ms = time_loop(step, steps, warmup)
+        res[name] = {"e2e_us": round(ms * 1e3, 2), "positions_per_s": round(s.R / (ms * 1e-3), 1)}
+    return res
+
+
+def measure_dynconv(device: str, steps: int, warmup: int) -> dict:
+    """The grouped dynamic depthwise convolution at the serving block shape: 64 blocks of the
+    verified token + 16 draft rows, hidden size 4096, 2 taps, groups of 16, bf16."""
+    import torch
+    import dflash2_draft_candidate_amd as d2
+    nb, T, C, K, G = 64, 17, 4096, 2, 16
+    g = torch.Generator().manual_seed(11)
+    x = torch.randn((nb, T, C), generator=g).to(torch.bfloat16).to(device)
+    base = (0.5 * torch.randn((K, C), generator=g)).to(torch.bfloat16).to(device)
+    dyn = (0.1 * torch.randn((nb, T, K, C // G), generator=g)).to(torch.bfloat16).to(device)
+    y = torch.empty_like(x)
+    # the kernel lasts a few microseconds, less than a Python call: time it inside a HIP graph
+    # of `reps` launches, replayed, so the host's launch cost stays out of the measurement
+    reps = 50
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        d2.dynconv(x, base, dyn, G, out=y)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            d2.dynconv(x, base, dyn, G, out=y)
+    ms = time_loop(lambda i: graph.replay(), max(1, steps // 10), warmup) / reps
+    nbytes = 2 * (2 * nb * T * C + nb * T * K * (C // G) + K * C)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"shape": {"n_blocks": nb, "T": T, "C": C, "K": K, "group": G, "dtype": "bf16"},
+            "launch_us": round(ms * 1e3, 2), "algorithmic_bytes": nbytes, "gbs": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def cpu_baseline(name: str, min_seconds: float = 12.0, max_passes: int = 64) -> dict:
@@ -324,7 +378,12 @@ def main():
         return
 
     main_res = measure(args.workload, device, args.steps, args.warmup)
-    s = main_res.pop("_workload").s
+    main_w = main_res.pop("_workload")
+    s = main_w.s
+    extras = {"walk_modes": measure_modes(main_w, args.steps, args.warmup),
+              "dynconv": measure_dynconv(device, args.steps, args.warmup)}
+    log(f"[bench] extras: {extras}")
+    del main_w
     log(f"[bench] {args.workload}: {main_res}")
     per_config = {args.workload: main_res}
     if not args.no_per_config:
@@ -367,6 +426,7 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload)
     line["per_config"] = per_config
+    line["extras"] = extras
     print(json.dumps(line), flush=True)
 
 

@@ -57,11 +57,13 @@ _lib.dflash2_walk_ex.restype = _ci
 _lib.dflash2_select_ex.argtypes = [_vp, _ci, _vp, _ci, _vp, _vp, _vp, _ci, _vp] + [_ci] * 6 + \
     [_cf, _vp, _cf, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.dflash2_select_ex.restype = _ci
+_lib.dflash2_dynconv.argtypes = [_vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _vp]
+_lib.dflash2_dynconv.restype = _ci
 
 EXPORTS = ("dflash2_version", "dflash2_status_string", "dflash2_workspace_bytes",
            "dflash2_select", "dflash2_topk_lse_workspace_bytes", "dflash2_topk_lse",
            "dflash2_gate_workspace_bytes", "dflash2_gate", "dflash2_lattice", "dflash2_walk",
-           "dflash2_select_ex", "dflash2_walk_ex")
+           "dflash2_select_ex", "dflash2_walk_ex", "dflash2_dynconv")
 
 
 class Dflash2Error(RuntimeError):
@@ -279,3 +281,21 @@ def walk_ex(edges: torch.Tensor, cand_ids: torch.Tensor, temperature: float = 0.
                               _stream(dev))
     _check(rc, "dflash2_walk_ex")
     return path, idx, dlen
+
+
+def dynconv(x: torch.Tensor, base: torch.Tensor, dyn: torch.Tensor, group: int,
+            out: torch.Tensor | None = None):
+    """Grouped dynamic depthwise convolution of the draft blocks: x [nb,T,C], base [K,C],
+    dyn [nb,T,K,C/group] (one dtype) -> y [nb,T,C] of x's dtype."""
+    _contig(x, base, dyn)
+    nb, T, C = x.shape
+    K = base.shape[0]
+    if base.shape != (K, C) or C % group != 0 or dyn.shape != (nb, T, K, C // group):
+        raise ValueError("inconsistent shapes")
+    if base.dtype != x.dtype or dyn.dtype != x.dtype:
+        raise TypeError("x, base and dyn must share a dtype")
+    y = torch.empty_like(x) if out is None else out
+    rc = _lib.dflash2_dynconv(_ptr(x), _ptr(base), _ptr(dyn), _dtype(x), nb, T, C, K, group,
+                              _ptr(y), _stream(x.device))
+    _check(rc, "dflash2_dynconv")
+    return y

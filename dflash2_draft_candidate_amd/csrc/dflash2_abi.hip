@@ -162,6 +162,18 @@ int dflash2_walk_ex(const float *edges, const int32_t *cand_ids, int B, int L, i
                                   static_cast<hipStream_t>(stream), &mode));
 }
 
+int dflash2_dynconv(const void *x, const void *base, const void *dyn, int dtype, int n_blocks,
+                    int T, int C, int K, int group, void *y, void *stream) {
+    if (n_blocks < 1 || T < 1 || C < 1 || K < 1 || K > DFLASH2_MAX_CONV_TAPS || group < 1 ||
+        C % group != 0 || !dtype_ok(dtype) ||
+        (int64_t)n_blocks * T * ((C + 255) / 256) > INT_MAX)  // one-dimensional grid
+        return DFLASH2_ERR_INVALID_ARG;
+    int rc = check_ptrs({x, base, dyn, y});
+    if (rc) return rc;
+    return hip_status(launch_dynconv(x, base, dyn, dtype, n_blocks, T, C, K, group, y,
+                                     static_cast<hipStream_t>(stream)));
+}
+
 size_t dflash2_workspace_bytes(int B, int L, int V, int H, int r, int k) {
     if (B < 1 || L < 1 || H < 1 || r < 1 || r > DFLASH2_MAX_R || rows_of(B, L) > INT_MAX ||
         check_rows((int)rows_of(B, L), V, k) != DFLASH2_OK)

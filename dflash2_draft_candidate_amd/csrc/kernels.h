@@ -71,4 +71,8 @@ hipError_t launch_walk(const float *edges, const int32_t *cand_ids, int B, int L
                        int32_t *path, int32_t *path_idx, hipStream_t stream,
                        const WalkMode *mode = nullptr);
 
+// ---- grouped dynamic depthwise convolution of the draft blocks ------------------------------
+hipError_t launch_dynconv(const void *x, const void *base, const void *dyn, int dtype, int nb,
+                          int Tn, int C, int K, int G, void *y, hipStream_t stream);
+
 }  // namespace dflash2

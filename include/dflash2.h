@@ -47,6 +47,7 @@ extern "C" {
 #define DFLASH2_MAX_K 64  /* largest top-k */
 #define DFLASH2_MAX_R 256 /* largest codebook rank r */
 #define DFLASH2_MAX_V (1 << 28) /* largest vocabulary (a row's bytes stay within 32-bit offsets) */
+#define DFLASH2_MAX_CONV_TAPS 8 /* largest kernel of dflash2_dynconv */
 
 typedef enum dflash2_dtype {
     DFLASH2_F32 = 0,  /* IEEE binary32 */
@@ -188,6 +189,32 @@ int dflash2_walk(const float *edges, const int32_t *cand_ids, int B, int L, int 
 int dflash2_walk_ex(const float *edges, const int32_t *cand_ids, int B, int L, int k,
                     float temperature, const float *uniforms, float p_min, int32_t *path,
                     int32_t *path_idx, int32_t *draft_len, void *stream);
+
+/*
+ * dflash2_dynconv - the grouped dynamic depthwise convolution of the draft blocks, one side of
+ *   a sublayer per call. Source: "DFlash 2: Keep Drafting Parallel" (inco.ai blog), section
+ *   "A Lightweight Local Convolution" (Conv_k(x)_t = k_{t,0} (.) x_t + k_{t,1} (.) x_{t-1}; each
+ *   coefficient a learned base kernel plus a correction from the hidden state, one per 16
+ *   channels; the first draft position reads the last verified token); "DFlash2 Lands in
+ *   llama.cpp" (ramgpt.org), section "Dynamic Local Convolution" (static weight per tap and
+ *   channel plus dynamic weight per position, tap and channel group; block-local, zero padded;
+ *   the same dynamic weights on both sides of a sublayer with one base kernel per side).
+ *
+ *   x      [n_blocks, T, C]          dtype, device. Row 0 of a block is the last verified token,
+ *                                    rows 1.. the draft positions.
+ *   base   [K, C]                    dtype, device. The side's static kernel.
+ *   dyn    [n_blocks, T, K, C/group] dtype, device. The dynamic correction of each output row,
+ *                                    tap and channel group (computed upstream from the hidden
+ *                                    state).
+ *   y      [n_blocks, T, C]          dtype, device, written in full:
+ *          y[b][t][c] = sum_{tap < K} (base[tap][c] + dyn[b][t][tap][c / group]) * x[b][t-tap][c],
+ *          x[b][t'][c] = 0 for t' < 0 (nothing crosses a block boundary). fp32 arithmetic; bf16
+ *          outputs are rounded to nearest even. y must not overlap x.
+ *   n_blocks, T, C >= 1; 1 <= K <= DFLASH2_MAX_CONV_TAPS; group >= 1 divides C.
+ * No workspace. Errors: DFLASH2_ERR_INVALID_ARG (sizes, dtype, NULL), DFLASH2_ERR_ALIGNMENT.
+ */
+int dflash2_dynconv(const void *x, const void *base, const void *dyn, int dtype, int n_blocks,
+                    int T, int C, int K, int group, void *y, void *stream);
 
 #ifdef __cplusplus
 }

@@ -42,6 +42,7 @@ def lib():
     L.dflash2_walk_ex.argtypes = [vp, vp, ci, ci, ci, cf, vp, cf, vp, vp, vp, vp]
     L.dflash2_select_ex.argtypes = [vp, ci, vp, ci, vp, vp, vp, ci, vp] + [ci] * 6 + \
         [cf, vp, cf, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dflash2_dynconv.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, vp, vp]
     L.dflash2_status_string.argtypes = [ci]
     L.dflash2_status_string.restype = ctypes.c_char_p
     return L
@@ -57,7 +58,7 @@ def test_header_declares_the_abi():
     names = declared_functions()
     for f in ("dflash2_select", "dflash2_workspace_bytes", "dflash2_status_string",
               "dflash2_topk_lse", "dflash2_gate", "dflash2_lattice", "dflash2_walk",
-              "dflash2_select_ex", "dflash2_walk_ex"):
+              "dflash2_select_ex", "dflash2_walk_ex", "dflash2_dynconv"):
         assert f in names
 
 
@@ -150,6 +151,18 @@ def test_mode_entry_points_reject(lib):
     assert sx(p_min=nan) == EINVAL
     assert sx(T=1.0, u=MIS) == EALIGN
     assert sx(dlen=MIS) == EALIGN
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=0), EINVAL), (dict(K=9), EINVAL), (dict(G=0), EINVAL), (dict(G=5), EINVAL),
+    (dict(nb=0), EINVAL), (dict(T=0), EINVAL), (dict(C=0), EINVAL), (dict(dt=2), EINVAL),
+    (dict(x=None), EINVAL), (dict(y=None), EINVAL), (dict(dyn=MIS), EALIGN), (dict(y=MIS), EALIGN),
+])
+def test_dynconv_rejects(lib, kw, status):
+    a = dict(x=P, base=P, dyn=P, dt=BF16, nb=2, T=5, C=64, K=2, G=16, y=P)
+    a.update(kw)
+    assert lib.dflash2_dynconv(a["x"], a["base"], a["dyn"], a["dt"], a["nb"], a["T"], a["C"],
+                               a["K"], a["G"], a["y"], None) == status
 
 
 def test_binding_rejects_host_tensors():

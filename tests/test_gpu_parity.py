@@ -281,6 +281,60 @@ def test_walk_ex_greedy_matches_walk(lib):
     assert torch.equal(p0, p1) and torch.equal(i0, i1) and bool((dlen == 16).all())
 
 
+# ---------------------------------------------- grouped dynamic depthwise convolution (f3)
+
+CONV_CASES = [(64, 17, 4096, 2, 16, "bf16"), (32, 17, 5376, 2, 16, "bf16"),
+              (3, 5, 40, 3, 8, "f32"), (2, 9, 36, 2, 4, "f32"), (2, 7, 30, 2, 5, "f32"),
+              (1, 1, 8, 8, 8, "bf16"), (4, 4, 24, 8, 8, "f32"), (3, 6, 48, 2, 4, "bf16"),
+              (5, 33, 256, 4, 16, "bf16"), (1, 3, 1, 1, 1, "f32")]
+
+
+@pytest.mark.parametrize("nb,T,C,K,G,dt", CONV_CASES,
+                         ids=[f"nb{a}-T{b}-C{c}-K{d}-G{e}-{f}" for a, b, c, d, e, f in CONV_CASES])
+def test_dynconv(lib, ref, nb, T, C, K, G, dt):
+    log(f"dynconv nb={nb} T={T} C={C} K={K} G={G} {dt}")
+    rng = np.random.default_rng(nb * 7 + T * 3 + C + K + G)
+    x = store(rng.normal(0, 1, (nb, T, C)).astype(np.float32), dt)
+    base = store(rng.normal(0, 0.5, (K, C)).astype(np.float32), dt)
+    dyn = store(rng.normal(0, 0.1, (nb, T, K, C // G)).astype(np.float32), dt)
+    y = to_np(lib.dynconv(to_dev(x), to_dev(base), to_dev(dyn), G))
+    torch.cuda.synchronize()
+    want = ref.dynconv(x, base, dyn, G)
+    # |terms|: the same sum with absolute values bounds fp32's rounding of it
+    wide = lambda a: synth.bf16_to_f32(a).astype(np.float64) if dt == "bf16" else a.astype(np.float64)
+    mag = ref.dynconv(np.abs(wide(x)).astype(np.float32), np.abs(wide(base)).astype(np.float32),
+                      np.abs(wide(dyn)).astype(np.float32), G)
+    got = wide(y)
+    tol = 1e-6 * mag + (2.0 ** -8 * np.abs(want) if dt == "bf16" else 0.0) + 1e-30
+    bad = np.abs(got - want) > tol
+    assert not bad.any(), f"{bad.sum()} outside tolerance; worst {np.max(np.abs(got - want) - tol):.3e}"
+
+
+def test_dynconv_graph_replay(lib):
+    # the benchmark times the convolution inside a HIP graph: every replay, with eager work in
+    # between, must reproduce the eager result bit for bit
+    g = torch.Generator().manual_seed(3)
+    nb, T, C, K, G = 8, 17, 512, 2, 16
+    x = torch.randn((nb, T, C), generator=g).to(torch.bfloat16).to(DEV)
+    base = torch.randn((K, C), generator=g).to(torch.bfloat16).to(DEV)
+    dyn = (0.1 * torch.randn((nb, T, K, C // G), generator=g)).to(torch.bfloat16).to(DEV)
+    want = lib.dynconv(x, base, dyn, G)
+    y = torch.empty_like(x)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lib.dynconv(x, base, dyn, G, out=y)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lib.dynconv(x, base, dyn, G, out=y)
+    for i in range(4):
+        y.fill_(float(i + 1))           # eager work between the replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), want.view(torch.int16)), f"replay {i}"
+
+
 # ------------------------------------------------------------------------------- end to end
 
 def run_select(lib, x):
