@@ -107,6 +107,34 @@ __device__ __forceinline__ uint64_t wave_merge_desc(uint64_t a, uint64_t c, int 
     return m;
 }
 
+// ---- cross-lane reductions (DPP: no LDS round trip) -----------------------------------------
+
+constexpr int kDppXor1 = 0xB1;   // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;   // quad_perm [2, 3, 0, 1]
+constexpr int kDppRor4 = 0x124;  // row_ror:4
+constexpr int kDppRor8 = 0x128;  // row_ror:8
+
+// Sum over each row of 16 lanes, in every lane of the row (rotations: each lane adds the same
+// values in a different order; every partial is a sum of distinct lanes).
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRor8, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRor4, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppXor2, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppXor1, 0xF, 0xF, false));
+    return v;
+}
+
+// Sum over the wave, wave-uniform: the four row sums (taken from the rows' first lanes) added in
+// row order, so the result depends only on the lane values.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return ((r0 + r1) + r2) + r3;
+}
+
 // ---- logsumexp partial state ---------------------------------------------------------------
 // (ref, sum) stands for log2-domain reference `ref` and sum = sum_i 2^(x_i*log2e - ref):
 // logsumexp = (ref + log2(sum)) * ln 2. ref = -inf with sum = 0 is the empty state.

@@ -118,22 +118,7 @@ __device__ __forceinline__ uint32_t walk_key(float e, int j) {
     return value_key(e);
 }
 
-constexpr int kDppXor1 = 0xB1;   // quad_perm [1, 0, 3, 2]
-constexpr int kDppXor2 = 0x4E;   // quad_perm [2, 3, 0, 1]
-constexpr int kDppRor4 = 0x124;  // row_ror:4
-constexpr int kDppRor8 = 0x128;  // row_ror:8
-
 __device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
-
-// Sum over each row of 16 lanes, in every lane of the row (rotations: each lane adds the same
-// values in a different order; every partial is a sum of distinct lanes).
-__device__ __forceinline__ float row16_sum(float v) {
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRor8, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRor4, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppXor2, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppXor1, 0xF, 0xF, false));
-    return v;
-}
 
 // Maximum over each row of 16 lanes, in every lane of the row.
 __device__ __forceinline__ uint32_t row16_max(uint32_t v) {

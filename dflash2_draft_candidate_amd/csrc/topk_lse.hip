@@ -24,17 +24,21 @@
 //     chunk whose sum leaves the safe fp32 range (an element far above every seeded maximum)
 //     sends the unit down a slow exact path at the end.
 //   * top-k. A 64-bit key (order-preserving logit map above the inverted id) makes the candidate
-//     order one unsigned compare. Each wave keeps its 64 best keys of the unit sorted across its
-//     lanes. An element is admitted only if it beats the unit's threshold in LDS, which is always
-//     valid (k real elements at or above it): the largest single-wave k-th key, or the smallest
-//     over the W waves of their ceil(k / W)-th keys. A batch costs one compare per lane unless
-//     some lane's maximum reaches it; then each such lane's batch is staged in LDS and read back
-//     transposed (lane j <- element j), and each surviving candidate is inserted by ballot +
-//     popcount rank and a one-lane DPP shift.
+//     order one unsigned compare. The unit's oldest wave (its owner) keeps the unit's 64 best
+//     keys sorted across its lanes; the other waves queue their candidates to it through LDS
+//     (a wave that finds the queue full keeps them in a list of its own, merged at the end). An
+//     element is admitted only if it beats the unit's threshold in LDS, which is always valid
+//     (k real elements at or above it): the k-th key of a wave's list, or the seed below. A batch costs
+//     one compare per lane of the lane's term sum unless it reaches the threshold's term; then
+//     each such lane's batch is staged in LDS and read back transposed (lane j <- element j),
+//     and each surviving candidate is inserted by ballot + popcount rank and a one-lane DPP
+//     shift.
 //   * Seed. The threshold starts at the k-th largest of the lane maxima of the unit's waves over
 //     their first batches (k real elements reach it).
-//   * End. The unit's W lists are merged by a tree of bitonic merges (the top k of distinct keys
-//     is unique) and the unit's first wave writes the results. Deterministic throughout.
+//   * End. The owner keeps draining the queue until every wave of its unit has finished the
+//     stream; after a barrier each wave adds a fixed range of the unit's chunk sums, and the
+//     owner merges any kept lists (bitonic merge: the top k of distinct keys is unique), adds the
+//     partial sums in wave order and writes the results. Deterministic throughout.
 //   * Fused gate (bf16 activations, r <= 128). The selector's gate product is independent of
 //     the logits, so the top-k pass can carry it: workgroup t computes split-K tile t of
 //     hidden . W_sel (the same tiles, wave ranges and summation order as the stand-alone gate
@@ -61,7 +65,7 @@ constexpr float kSumLimit = 0x1p100f;     // a chunk sum above this leaves the f
 constexpr float kSumFloor = 0x1p-60f;     // so does a unit total below this
 constexpr float kTermMargin = 1.f - 0x1p-10f;  // v_exp_f32 is far more accurate than this
 constexpr int kMaxSumHits = 4;            // lanes the sum filter may flag before maxima decide
-constexpr int kQueue = 64;                // candidate queue slots per unit
+constexpr int kQueueSlots = 512;          // candidate queue slots per workgroup (G units share)
 constexpr int kSeedBatches = 3;           // batches per wave behind the seed (<= kRing)
 constexpr int kBufferWord3 = 0x00020000;  // gfx9-family buffer descriptor word 3 (raw data)
 constexpr int kNonTemporal = 2;           // cache policy: streaming data, read once
@@ -93,18 +97,20 @@ __device__ __forceinline__ uint64_t shift_up_one(uint64_t v) {
 // Per-workgroup state in LDS (besides the chunk sums).
 struct K1Shared {
     uint64_t tau[kMaxUnits];          // admission threshold of each unit
-    uint64_t queue[kMaxUnits][kQueue];  // candidates on their way to the unit's owner (0: empty)
+    uint64_t queue[kQueueSlots];      // candidates on their way to the units' owners (0: empty);
+                                      // unit q owns slots [q, q + 1) * kQueueSlots / G
     uint32_t q_tail[kMaxUnits];       // queue slots reserved so far
     uint32_t q_head[kMaxUnits];       // queue slots consumed by the owner so far
     uint32_t spilled;                 // bit s: slot s kept candidates in its own list
     uint64_t lists[kWaves * kWave];   // spilled lists, for the final merge
-    uint32_t seed_vals[kWaves * kWave];
+    uint32_t seed_vals[kWaves * kWave];  // seed maxima; after the stream: partial chunk sums
     float rag[kMaxUnits * kWave];     // the unit's ragged-end sums per lane
     u32x4 stage[kWaves][kU];          // per wave: one hit lane's batch, read back transposed
     uint32_t next_chunk[kMaxUnits];   // next chunk of the unit to hand out
     uint32_t seeded[kMaxUnits];       // waves of the unit that have published their seed
     uint32_t overflow[kMaxUnits];     // a chunk sum left the safe range
     uint32_t gate_arrived;            // gate waves that have stored their part of the tile
+    uint32_t done[kMaxUnits];         // waves of the unit that have finished the stream
 };
 
 // The gate tiles carried by the top-k pass: tile t = sp * mtiles + mt covers rows mt*16 ..
@@ -164,8 +170,9 @@ struct WaveTopk {
     float tau_v;           // logit of the threshold, for the cheap first test
     int k;
     uint64_t *shared_tau;  // the unit's threshold in LDS
-    uint64_t *queue;       // the unit's candidate queue
+    uint64_t *queue;       // the unit's candidate queue (qmask + 1 slots, a power of two)
     uint32_t *q_tail, *q_head;
+    uint32_t qmask;
     uint32_t head;         // owner: slots consumed
     bool owner;            // this wave keeps the unit's list
     bool spilled;          // a non-owner that had to keep candidates itself
@@ -216,9 +223,9 @@ __device__ __forceinline__ void accept(WaveTopk &w, uint64_t c, int lane) {
     pos = __builtin_amdgcn_readfirstlane(pos);
     const uint32_t head = __builtin_amdgcn_readfirstlane(
         __hip_atomic_load(w.q_head, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
-    if (pos - head < (uint32_t)kQueue) {  // the slot's previous occupant has been consumed
+    if (pos - head <= w.qmask) {  // the slot's previous occupant has been consumed
         if (lane == 0)
-            __hip_atomic_store(&w.queue[pos % kQueue], c, __ATOMIC_RELEASE,
+            __hip_atomic_store(&w.queue[pos & w.qmask], c, __ATOMIC_RELEASE,
                                __HIP_MEMORY_SCOPE_WORKGROUP);
     } else {  // full (the reserved slot stays 0, a hole the owner skips at the end)
         wave_insert(w, c, lane);
@@ -234,7 +241,7 @@ __device__ __forceinline__ void drain(WaveTopk &w, int lane, bool all) {
         __hip_atomic_load(w.q_tail, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
     while (w.head != tail) {
         const uint32_t n = min(tail - w.head, (uint32_t)kWave);
-        const uint32_t slot = (w.head + lane) % kQueue;
+        const uint32_t slot = (w.head + lane) & w.qmask;
         const uint64_t key = lane < (int)n ? __hip_atomic_load(&w.queue[slot], __ATOMIC_ACQUIRE,
                                                                __HIP_MEMORY_SCOPE_WORKGROUP)
                                            : 0ull;
@@ -478,8 +485,8 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     }
     if (threadIdx.x < kMaxUnits) sh.q_tail[threadIdx.x] = sh.q_head[threadIdx.x] = 0u;
     if (threadIdx.x == 0) sh.spilled = 0u;
-    for (int i = threadIdx.x; i < kMaxUnits * kQueue; i += kThreads) (&sh.queue[0][0])[i] = 0ull;
-    if (threadIdx.x < kMaxUnits) sh.seeded[threadIdx.x] = 0u;
+    for (int i = threadIdx.x; i < kQueueSlots; i += kThreads) sh.queue[i] = 0ull;
+    if (threadIdx.x < kMaxUnits) sh.seeded[threadIdx.x] = sh.done[threadIdx.x] = 0u;
     if (threadIdx.x == 0) sh.gate_arrived = 0u;
     __syncthreads();  // the only barrier before the stream (every wave arrives long before data)
 
@@ -571,7 +578,8 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     w.top = 0ull;
     w.k = k;
     w.shared_tau = &sh.tau[q];
-    w.queue = sh.queue[q];
+    w.qmask = (uint32_t)(kQueueSlots / G - 1);
+    w.queue = sh.queue + q * (kQueueSlots / G);
     w.q_tail = &sh.q_tail[q];
     w.q_head = &sh.q_head[q];
     w.head = 0u;
@@ -665,9 +673,28 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
         }
     }
 
-    // Every wave is done, so every reserved queue slot is final: the owner takes what is left in
-    // the queue and merges the lists of any wave that had to keep candidates itself.
+    // The owner keeps taking queued candidates until every wave of its unit has finished (the
+    // others never wait, so this ends), which leaves little for the pass after the barrier.
+    if (lane == 0)
+        __hip_atomic_fetch_add(&sh.done[q], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (w.owner) {
+        while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                   &sh.done[q], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) < (uint32_t)W) {
+            drain(w, lane, false);
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    // Every wave is done, so every reserved queue slot is final and every chunk sum is in LDS.
+    // Each wave of a unit adds a fixed range of its chunk sums (per lane, in chunk order); the
+    // owner takes what is left in the queue and merges the lists of any wave that had to keep
+    // candidates itself.
     __syncthreads();
+    float *psum = reinterpret_cast<float *>(sh.seed_vals);
+    if (active) {
+        float t = 0.f;
+        for (int c = nch * wv / W; c < nch * (wv + 1) / W; ++c) t += csums[c * kWave + lane];
+        psum[wave * kWave + lane] = t;
+    }
     if (w.spilled) {
         sh.lists[wave * kWave + lane] = w.top;
         if (lane == 0)
@@ -683,17 +710,17 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
         sp &= sp - 1u;
         w.top = wave_merge_desc(w.top, sh.lists[s * kWave + lane], lane);
     }
-    // The unit's logsumexp: chunk sums per lane in chunk order, then the ragged sums, then
-    // across lanes (fixed butterfly); lse = (R + log2 total) ln 2.
+    // The unit's logsumexp: the waves' partial sums per lane in wave order, then the ragged
+    // sums, then across lanes (fixed order); lse = (R + log2 total) ln 2.
     float ref = R, sum = 0.f;
     bool fast =
         __hip_atomic_load(&sh.overflow[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u;
     if (fast) {
         float t = 0.f;
-        for (int c = 0; c < nch; ++c) t += csums[c * kWave + lane];
-        t += sh.rag[q * kWave + lane];
 #pragma unroll
-        for (int off = kWave / 2; off > 0; off >>= 1) t += __shfl_xor(t, off, kWave);
+        for (int i = 0; i < W; ++i) t += psum[unit_slot<G>(q, i) * kWave + lane];
+        t += sh.rag[q * kWave + lane];
+        t = wave_sum(t);
         sum = t;
         fast = t >= kSumFloor;  // every term far below 1: too few significant bits left
     }
