@@ -4,11 +4,12 @@
 // A wave accumulates a 16-row tile over a range of H in steps of 32 with
 // v_mfma_f32_16x16x32_bf16 (fp32 accumulation):
 //   * A fragments (8 consecutive h of one row) are 16-byte loads of `hidden`;
-//   * W_sel is [H, r] (r contiguous), but a B fragment needs 8 consecutive h of one column. Each
-//     lane loads 4-byte column pairs (2c, 2c+1) of its 8 rows of W_sel and repacks the low halves
-//     into the fragment of one output tile and the high halves into the next, so the output
-//     columns of tile pair (2p, 2p+1) at lane position m are 32p + 2m and 32p + 2m + 1. Every
-//     load is independent: a batch of steps is issued before any MFMA runs.
+//   * W_sel is [H, r] (r contiguous), but a B fragment needs 8 consecutive h of one column. Lane
+//     position m loads the NT contiguous columns NT*m .. NT*m + NT - 1 of each of its 8 rows in one
+//     vector load (16 lanes cover a row of r = 16 * NT columns: coalesced), and the fragment of
+//     tile t takes column NT*m + t from the 8 rows (low halves of the column pairs for even t,
+//     high halves for odd t). So the output column of tile t at lane position m is NT*m + t.
+//     Every load is independent: a batch of steps is issued before any MFMA runs.
 // Sources: "DFlash 2: Keep Drafting Parallel" (inco.ai blog), section "A Lightweight Path
 // Selector" (context gate H(h_t)); "DFlash2 Lands in llama.cpp" (ramgpt.org), section "What
 // llama.cpp Actually Builds for the Selector" (hidden state through the selector-hidden weight).
@@ -27,21 +28,22 @@ constexpr int kStepK = 32;     // H per MFMA
 __device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
 __device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
 
-// Output column of MFMA tile t at lane position m (NT >= 2: column pairs; NT == 1: identity).
+// Output column of MFMA tile t at lane position m.
 template <int NT>
 __device__ __forceinline__ int out_col(int t, int m) {
-    return NT == 1 ? m : 32 * (t >> 1) + 2 * m + (t & 1);
+    return NT * m + t;
 }
 
 template <int NT>
 struct Step {
     static constexpr int NP = NT == 1 ? 1 : NT / 2;  // column pairs per lane
     u32x4 a;                                        // A fragment
-    uint32_t w[8][NP];                              // W rows k0+8g+i, column pair p
+    uint32_t w[8][NP];                              // W rows k0+8g+i, columns NT*m + 2p, +1
 };
 
 // Loads of one 32-wide step. FAST (wave-uniform): the step lies inside H, H % 8 == 0 and r is
-// exactly the padded tile width, so every load is unconditional (rows past R read row R-1 and
+// exactly the padded tile width (so W_sel rows are 2*NT*16-byte multiples and each lane's
+// columns are one aligned vector), so every load is unconditional (rows past R read row R-1 and
 // are discarded at the store); no branch separates the loads, and they all stay in flight.
 template <int NT, bool FAST>
 __device__ __forceinline__ void load_step(Step<NT> &s, const uint16_t *hrow, bool row_ok,
@@ -52,10 +54,14 @@ __device__ __forceinline__ void load_step(Step<NT> &s, const uint16_t *hrow, boo
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const uint16_t *wrow = W + (int64_t)(kc + i) * r;
+            if (NT == 1) {
+                s.w[i][0] = wrow[m];
+            } else {
+                typedef uint32_t row_t __attribute__((ext_vector_type(Step<NT>::NP)));
+                const row_t v = *reinterpret_cast<const row_t *>(wrow + NT * m);
 #pragma unroll
-            for (int p = 0; p < Step<NT>::NP; ++p)
-                s.w[i][p] = NT == 1 ? (uint32_t)wrow[m]
-                                    : *reinterpret_cast<const uint32_t *>(wrow + 32 * p + 2 * m);
+                for (int p = 0; p < Step<NT>::NP; ++p) s.w[i][p] = v[p];
+            }
         }
         return;
     }
@@ -72,7 +78,7 @@ __device__ __forceinline__ void load_step(Step<NT> &s, const uint16_t *hrow, boo
             if (NT == 1) {
                 s.w[i][p] = (kr < H && m < r) ? wrow[m] : 0u;
             } else {
-                const int c = 32 * p + 2 * m;
+                const int c = NT * m + 2 * p;
                 s.w[i][p] = (kr < H && c < r ? wrow[c] : 0u) |
                             ((kr < H && c + 1 < r ? (uint32_t)wrow[c + 1] : 0u) << 16);
             }
@@ -103,7 +109,7 @@ __device__ __forceinline__ void mma_step(const Step<NT> &s, f32x4 *acc) {
 }
 
 // Steps whose loads are issued together, by tile count (bounded by registers).
-template <int NT> constexpr int batch_steps() { return NT <= 4 ? 4 : (NT == 8 ? 2 : 1); }
+template <int NT> constexpr int batch_steps() { return NT <= 2 ? 4 : (NT == 4 ? 2 : 1); }
 
 
 // Steps [s0, s1) of wave q of the nq waves that share a tile's H (q = split * 4 + wave).

@@ -44,7 +44,7 @@
 //     hidden . W_sel (the same tiles, wave ranges and summation order as the stand-alone gate
 //     kernel) on four of its waves (one per SIMD) before they join the stream; the last of the
 //     four to finish sums their parts through LDS and stores the tile. The work sharing lets the
-//     other twelve waves absorb the delay.
+//     other twelve waves absorb the delay. Tiles are numbered XCD by XCD (see xcd_major).
 #include "device_common.h"
 #include "gate_tile.h"
 #include "kernels.h"
@@ -110,7 +110,11 @@ struct K1Shared {
     uint32_t seeded[kMaxUnits];       // waves of the unit that have published their seed
     uint32_t overflow[kMaxUnits];     // a chunk sum left the safe range
     uint32_t gate_arrived;            // gate waves that have stored their part of the tile
-    uint32_t done[kMaxUnits];         // waves of the unit that have finished the stream
+    int64_t unit_c0[kMaxUnits];       // each unit's first whole vector,
+    int32_t unit_nv[kMaxUnits];       // its whole vectors,
+    int32_t unit_idb0[kMaxUnits];     // the id of its first vector's first element,
+    uint32_t unit_nch[kMaxUnits];     // and its chunks (0: no unit)
+    uint32_t done_all;                // waves that have finished the stream
 };
 
 // The gate tiles carried by the top-k pass: tile t = sp * mtiles + mt covers rows mt*16 ..
@@ -130,12 +134,21 @@ template <int G> constexpr int gate_first_wave() { return G == 8 ? 8 : 4; }
 template <int NT>
 constexpr size_t gate_red_floats() { return NT == 0 ? 0 : (size_t)kGateWaves * 16 * (NT * 16 + 1); }
 
+// Workgroups are dispatched to the XCDs round-robin (workgroup g on XCD g % kXcds). Numbering
+// the gate tiles XCD by XCD gives each XCD a run of consecutive tiles (m-tiles of one or two
+// W_sel slices), so each XCD's L2 fetches the W_sel slices it needs once instead of every
+// XCD fetching all of W_sel for every m-tile.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_major(int g, int n) {
+    return n % kXcds == 0 ? (g % kXcds) * (n / kXcds) + g / kXcds : g;
+}
+
 // Wave gw (0..3) of the workgroup's gate tile; the last of the four stores the tile.
 template <int NT>
 __device__ __forceinline__ void gate_tile_part(const GateJob &gj, int gw, int lane, float *red,
                                             uint32_t *arrived) {
     constexpr int PITCH = NT * 16 + 1;
-    const int t = blockIdx.x;
+    const int t = xcd_major(blockIdx.x, gridDim.x);
     if (t >= gj.mtiles * gj.splits) return;
     const int mt = t % gj.mtiles, sp = t / gj.mtiles;
     int s0, s1;
@@ -175,6 +188,7 @@ struct WaveTopk {
     uint32_t qmask;
     uint32_t head;         // owner: slots consumed
     bool owner;            // this wave keeps the unit's list
+    bool home;             // the unit being processed is the wave's own (else it helps another)
     bool spilled;          // a non-owner that had to keep candidates itself
 };
 
@@ -210,32 +224,56 @@ __device__ __forceinline__ void wave_insert(WaveTopk &w, uint64_t c, int lane) {
     raise_tau(w, lane_value(w.top, w.k - 1), lane);
 }
 
-// A candidate above the threshold: the owner inserts it; another wave queues it for the owner,
-// or, if the queue is full, keeps it in its own list (merged at the end). Queueing never waits.
+// Reserve the next queue slot if the queue has room (its previous occupant consumed).
+__device__ __forceinline__ bool try_reserve(WaveTopk &w, int lane, uint32_t &pos) {
+    uint32_t ok = 0u, p = 0u;
+    if (lane == 0) {
+        const uint32_t head =
+            __hip_atomic_load(w.q_head, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        uint32_t tail = __hip_atomic_load(w.q_tail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        while (tail - head <= w.qmask) {
+            if (__hip_atomic_compare_exchange_strong(w.q_tail, &tail, tail + 1u, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_WORKGROUP)) {
+                ok = 1u;
+                p = tail;
+                break;
+            }
+        }
+    }
+    pos = __builtin_amdgcn_readfirstlane(p);
+    return __builtin_amdgcn_readfirstlane(ok) != 0u;
+}
+
+// A candidate above the threshold: the owner inserts it; another wave queues it for the owner.
+// If the queue is full, a wave of the unit keeps it in its own list (merged at the end), and a
+// wave helping from another unit waits for room (the owner drains until every wave is done).
+// A reserved slot is written at once, so the queue never holds a hole.
 __device__ __forceinline__ void accept(WaveTopk &w, uint64_t c, int lane) {
     if (w.owner) {
         wave_insert(w, c, lane);
         return;
     }
-    uint32_t pos = 0u;
-    if (lane == 0)
-        pos = __hip_atomic_fetch_add(w.q_tail, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    pos = __builtin_amdgcn_readfirstlane(pos);
-    const uint32_t head = __builtin_amdgcn_readfirstlane(
-        __hip_atomic_load(w.q_head, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
-    if (pos - head <= w.qmask) {  // the slot's previous occupant has been consumed
-        if (lane == 0)
-            __hip_atomic_store(&w.queue[pos & w.qmask], c, __ATOMIC_RELEASE,
-                               __HIP_MEMORY_SCOPE_WORKGROUP);
-    } else {  // full (the reserved slot stays 0, a hole the owner skips at the end)
-        wave_insert(w, c, lane);
-        w.spilled = true;
+    for (;;) {
+        uint32_t pos;
+        if (try_reserve(w, lane, pos)) {
+            if (lane == 0)
+                __hip_atomic_store(&w.queue[pos & w.qmask], c, __ATOMIC_RELEASE,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+            return;
+        }
+        if (w.home) {
+            wave_insert(w, c, lane);
+            w.spilled = true;
+            return;
+        }
+        __builtin_amdgcn_s_sleep(1);
     }
 }
 
 // Owner: insert the queued candidates, consuming the written prefix of the queue (a reserved
 // slot not yet written stops it until the next call). `all`: after the stream, when every
-// reserved slot is final: take every written slot and skip holes.
+// reserved slot is written: take them all.
 __device__ __forceinline__ void drain(WaveTopk &w, int lane, bool all) {
     const uint32_t tail = __builtin_amdgcn_readfirstlane(
         __hip_atomic_load(w.q_tail, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
@@ -486,8 +524,14 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     if (threadIdx.x < kMaxUnits) sh.q_tail[threadIdx.x] = sh.q_head[threadIdx.x] = 0u;
     if (threadIdx.x == 0) sh.spilled = 0u;
     for (int i = threadIdx.x; i < kQueueSlots; i += kThreads) sh.queue[i] = 0ull;
-    if (threadIdx.x < kMaxUnits) sh.seeded[threadIdx.x] = sh.done[threadIdx.x] = 0u;
-    if (threadIdx.x == 0) sh.gate_arrived = 0u;
+    if (threadIdx.x < kMaxUnits) sh.seeded[threadIdx.x] = 0u;
+    if (threadIdx.x == 0) sh.gate_arrived = sh.done_all = 0u;
+    if (wv == 0 && lane == 0) {
+        sh.unit_c0[q] = ur.c0;
+        sh.unit_nv[q] = nv;
+        sh.unit_idb0[q] = (int32_t)(ur.c0 * EV - ur.g0);
+        sh.unit_nch[q] = (uint32_t)nch;
+    }
     __syncthreads();  // the only barrier before the stream (every wave arrives long before data)
 
     if constexpr (NTG > 0) {
@@ -497,20 +541,23 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     }
 
     const int voff = lane * 16;
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+    // Issue side: the unit being loaded (the wave's own; once it has no chunks left, a wave other
+    // than the owner helps the unit of the workgroup with the most chunks left).
+    int iq = q, i_nb = nb, i_nch = nch;
+    __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<u32x4 *>(reinterpret_cast<const u32x4 *>(logits) + ur.c0), 0, nv * 16,
         kBufferWord3);
 
     // Ring slots: data and (wave-uniform) metadata: batch index, chunk, flags (1 valid, 2 first
-    // batch of its chunk, 4 last).
+    // batch of its chunk, 4 last; bits 8 up: the unit).
     u32x4 ring[kRing][kU];
     int s_b[kRing], s_c[kRing], s_flags[kRing];
 #pragma unroll
     for (int j = 0; j < kRing; ++j) s_b[j] = s_c[j] = s_flags[j] = 0;
 
-    // Issue side: the chunk being issued and the next batch in it. The wave's first P chunks are
-    // wv, wv + W, ...; later ones come from the unit's counter (which starts at W * P),
-    // requested one chunk ahead. Chunk ids only grow, so every wave runs out of work.
+    // The wave's first P chunks of its own unit are wv, wv + W, ...; later ones come from the
+    // unit's counter (which starts at W * P), requested one chunk ahead. Chunk ids only grow, so
+    // every wave runs out of work.
     int cur_c = 0, cur_i = 0, cur_n = 0, taken = 0;
     uint32_t pending = 0u;
     auto take_chunk = [&]() -> int {
@@ -521,27 +568,64 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
             c = __builtin_amdgcn_readfirstlane(pending);
         ++taken;
         if (taken >= P && lane == 0)
-            pending = __hip_atomic_fetch_add(&sh.next_chunk[q], 1u, __ATOMIC_RELAXED,
+            pending = __hip_atomic_fetch_add(&sh.next_chunk[iq], 1u, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_WORKGROUP);
-        return c < nch ? c : -1;
+        return c < i_nch ? c : -1;
     };
+    // Move the issue side to the unit with the most chunks left; false if none has any.
+    const bool can_help = !(active && wv == 0);
+    auto switch_unit = [&]() -> bool {
+        if (!can_help) return false;
+        int best = -1;
+        uint32_t most = 0u;
+        for (int u = 0; u < G; ++u) {
+            const uint32_t n = __builtin_amdgcn_readfirstlane(sh.unit_nch[u]);
+            const uint32_t next = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                &sh.next_chunk[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+            const uint32_t left = next < n ? n - next : 0u;
+            if (left > most) {
+                most = left;
+                best = u;
+            }
+        }
+        if (best < 0) return false;
+        iq = best;
+        const int inv = __builtin_amdgcn_readfirstlane(sh.unit_nv[iq]);
+        i_nb = (inv + kStep - 1) / kStep;
+        i_nch = __builtin_amdgcn_readfirstlane(sh.unit_nch[iq]);
+        rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<u32x4 *>(reinterpret_cast<const u32x4 *>(logits) +
+                                (int64_t)uniform64((uint64_t)sh.unit_c0[iq])),
+            0, inv * 16, kBufferWord3);
+        taken = P;  // counter chunks only
+        if (lane == 0)
+            pending = __hip_atomic_fetch_add(&sh.next_chunk[iq], 1u, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_WORKGROUP);
+        return true;
+    };
+    // Load the next batch of the issue side's unit into slot j; once the unit has no chunks left
+    // the slot stays empty and the issue side is stalled until the main loop moves it (empty
+    // slots then follow every loaded one in processing order, so they are refilled in index
+    // order).
+    bool stalled = false;
     auto issue = [&](int j) {
         if (cur_i == cur_n) {
-            const int c = take_chunk();
+            const int c = stalled ? -1 : take_chunk();
             if (c < 0) {
                 s_flags[j] = 0;
                 cur_i = cur_n = 0;
+                stalled = true;
                 return;
             }
             cur_c = c;
             cur_i = 0;
-            cur_n = min(CB, nb - c * CB);
+            cur_n = min(CB, i_nb - c * CB);
         }
         const int b = cur_c * CB + cur_i;
         load_batch(rsrc, voff, b, ring[j]);
         s_b[j] = b;
         s_c[j] = cur_c;
-        s_flags[j] = 1 | (cur_i == 0 ? 2 : 0) | (cur_i == cur_n - 1 ? 4 : 0);
+        s_flags[j] = 1 | (cur_i == 0 ? 2 : 0) | (cur_i == cur_n - 1 ? 4 : 0) | (iq << 8);
         ++cur_i;
     };
 
@@ -561,7 +645,7 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
         float m = fmaxf(xh, xt);
 #pragma unroll
         for (int j = 0; j < kSeedBatches; ++j) {
-            if (s_flags[j] & 1) {
+            if ((s_flags[j] & 1) && (s_flags[j] >> 8) == q) {
                 float x[kU * EV], bmax;
                 const int nvalid = min(kStep, nv - s_b[j] * kStep);
                 if (nvalid < kStep)
@@ -584,6 +668,7 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     w.q_head = &sh.q_head[q];
     w.head = 0u;
     w.owner = active && wv == 0;  // the unit's oldest wave keeps its list
+    w.home = true;
     w.spilled = false;
     set_tau(w, 0ull);
     // Threshold seed, with no barrier: the wave starts from the k-th largest of its own 64 lane
@@ -638,18 +723,39 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
                              (int32_t)(ur.t0 - ur.g0), 1, lane, stage);
     }
 
-    // Main loop: process the oldest slot, then issue the next batch into it.
+    // Main loop: process the oldest slot, then issue the next batch into it. The processing side
+    // follows the slots' unit: when it changes, the wave joins the other unit's queue and
+    // threshold (it never owns a list there).
     float csum = 0.f;
-    const int32_t idb0 = (int32_t)(ur.c0 * EV - ur.g0);
+    int pq = q, p_nv = nv;
+    int32_t idb0 = (int32_t)(ur.c0 * EV - ur.g0);
     uint64_t te_key = ~0ull;  // the threshold t_e was computed for
     float t_e = 0.f;
     bool more = true;
     while (more) {
+        if (stalled && switch_unit()) {
+            stalled = false;
+#pragma unroll
+            for (int j = 0; j < kRing; ++j)
+                if (!(s_flags[j] & 1)) issue(j);
+        }
 #pragma unroll
         for (int j = 0; j < kRing; ++j) {
             if (!(s_flags[j] & 1)) {
                 more = false;
                 break;
+            }
+            if ((s_flags[j] >> 8) != pq) {
+                pq = s_flags[j] >> 8;
+                p_nv = __builtin_amdgcn_readfirstlane(sh.unit_nv[pq]);
+                idb0 = __builtin_amdgcn_readfirstlane(sh.unit_idb0[pq]);
+                w.shared_tau = &sh.tau[pq];
+                w.queue = sh.queue + pq * (kQueueSlots / G);
+                w.q_tail = &sh.q_tail[pq];
+                w.q_head = &sh.q_head[pq];
+                w.home = pq == q;
+                set_tau(w, 0ull);
+                te_key = ~0ull;
             }
             if (w.owner) drain(w, lane, false);
             pull_tau(w);
@@ -659,27 +765,29 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
             }
             if (s_flags[j] & 2) csum = 0.f;
             const int b = s_b[j];
-            const int nvalid = min(kStep, nv - b * kStep);
+            const int nvalid = min(kStep, p_nv - b * kStep);
             const int32_t id_base = idb0 + b * kStep * EV;
             if (nvalid < kStep)
                 batch<T, true>(ring[j], nvalid, id_base, R, t_e, csum, w, lane, stage);
             else
                 batch<T, false>(ring[j], kStep, id_base, R, t_e, csum, w, lane, stage);
             if (s_flags[j] & 4) {
-                csums[s_c[j] * kWave + lane] = csum;
-                if (__ballot(!(csum <= kSumLimit)) != 0ull && lane == 0) sh.overflow[q] = 1u;
+                chunk_sums[((size_t)pq * nch_max + s_c[j]) * kWave + lane] = csum;
+                if (__ballot(!(csum <= kSumLimit)) != 0ull && lane == 0) sh.overflow[pq] = 1u;
             }
             issue(j);
         }
     }
 
-    // The owner keeps taking queued candidates until every wave of its unit has finished (the
-    // others never wait, so this ends), which leaves little for the pass after the barrier.
+    // The owner keeps taking queued candidates until every wave of the workgroup has finished
+    // (any of them may help its unit; none waits on anything but an owner's draining, so this
+    // ends), which leaves little for the pass after the barrier.
     if (lane == 0)
-        __hip_atomic_fetch_add(&sh.done[q], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_add(&sh.done_all, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (w.owner) {
         while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
-                   &sh.done[q], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) < (uint32_t)W) {
+                   &sh.done_all, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) <
+               (uint32_t)kWaves) {
             drain(w, lane, false);
             __builtin_amdgcn_s_sleep(2);
         }
@@ -692,7 +800,16 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     float *psum = reinterpret_cast<float *>(sh.seed_vals);
     if (active) {
         float t = 0.f;
-        for (int c = nch * wv / W; c < nch * (wv + 1) / W; ++c) t += csums[c * kWave + lane];
+        int c = nch * wv / W;
+        const int c1 = nch * (wv + 1) / W;
+        for (; c + 8 <= c1; c += 8) {  // loads issued together, added in chunk order
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = csums[(c + i) * kWave + lane];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) t += v[i];
+        }
+        for (; c < c1; ++c) t += csums[c * kWave + lane];
         psum[wave * kWave + lane] = t;
     }
     if (w.spilled) {
