@@ -78,11 +78,13 @@ class Oracle:
                                                  _c_dbl_p, ctypes.c_double, _c_int_p, _c_int_p,
                                                  _c_int_p, _c_dbl_p, _c_dbl_p]
         self.lib.dflash2_ref_dynconv.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, _c_dbl_p]
+        self.lib.dflash2_ref_lmhead_topk.argtypes = [vp, vp, ci, ci, ci, ci, ci, _c_int_p, _c_dbl_p,
+                                                     _c_dbl_p, _c_dbl_p]
         self.lib.dflash2_ref_select.argtypes = [vp, ci, vp, ci, vp, vp, vp, ci, _c_int_p, ci, ci, ci,
                                                 ci, ci, ci, _c_int_p, _c_dbl_p, _c_dbl_p, _c_int_p,
                                                 _c_dbl_p, _c_int_p, _c_dbl_p, _c_dbl_p]
         for f in ("dflash2_ref_topk_lse", "dflash2_ref_gate", "dflash2_ref_lattice",
-                  "dflash2_ref_walk", "dflash2_ref_select"):
+                  "dflash2_ref_walk", "dflash2_ref_select", "dflash2_ref_lmhead_topk"):
             getattr(self.lib, f).restype = ctypes.c_int
 
     @staticmethod
@@ -103,6 +105,28 @@ class Oracle:
                                            lse.ctypes.data_as(_c_dbl_p))
         self._check(rc, "topk_lse")
         return ids, unary, lse
+
+    def lmhead_topk(self, hidden: np.ndarray, W_lm: np.ndarray, k: int, want_logits=False):
+        """hidden [R, H], W_lm [V, H] (same dtype) -> cand_ids [R,k] int32, unary [R,k], lse [R]
+        (and the logits [R, V] float64 when want_logits)."""
+        hidden = np.ascontiguousarray(hidden)
+        W_lm = np.ascontiguousarray(W_lm)
+        if hidden.dtype != W_lm.dtype:
+            raise TypeError("hidden and W_lm share one dtype")
+        R, H = hidden.shape
+        V, H2 = W_lm.shape
+        if H2 != H:
+            raise ValueError("W_lm must be [V, H]")
+        ids = np.zeros((R, k), np.int32)
+        unary = np.zeros((R, k), np.float64)
+        lse = np.zeros((R,), np.float64)
+        x = np.zeros((R, V), np.float64) if want_logits else None
+        rc = self.lib.dflash2_ref_lmhead_topk(
+            _ptr(hidden), _ptr(W_lm), dtype_code(hidden), R, H, V, k,
+            ids.ctypes.data_as(_c_int_p), unary.ctypes.data_as(_c_dbl_p),
+            lse.ctypes.data_as(_c_dbl_p), None if x is None else x.ctypes.data_as(_c_dbl_p))
+        self._check(rc, "lmhead_topk")
+        return (ids, unary, lse, x) if want_logits else (ids, unary, lse)
 
     def gate(self, hidden: np.ndarray, W_sel: np.ndarray):
         """hidden [R, H], W_sel [H, r] (same dtype) -> g [R, r] float64."""

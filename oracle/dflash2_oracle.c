@@ -136,6 +136,86 @@ int dflash2_ref_topk_lse(const void *logits, int dtype, int R, int V, int k,
 }
 
 /*
+ * The LM-head product with the top-k pass over it (the drafter's logits, never stored by the GPU
+ * path): x[i][v] = sum_h hidden[i][h] * W_lm[v][h], then the per-row top-k and logsumexp of x as
+ * defined for dflash2_ref_topk_lse. Sources: "DFlash2 Lands in llama.cpp" (ramgpt.org), section
+ * "What llama.cpp Actually Builds for the Selector" (the per-position top-k over the logits of
+ * the drafter's full-vocabulary projection).
+ * hidden: [R, H], W_lm: [V, H] (both dtype), cand_ids: [R, k], unary: [R, k], lse: [R] (may be
+ * NULL), logits: [R, V] (may be NULL; receives x).
+ */
+int dflash2_ref_lmhead_topk(const void *hidden, const void *W_lm, int dtype, int R, int H, int V,
+                            int k, int32_t *cand_ids, double *unary, double *lse, double *logits)
+{
+    if (!hidden || !W_lm || !cand_ids || !unary || !dtype_ok(dtype) || R < 0 || H < 1 || V < 1 ||
+        k < 1 || k > V)
+        return ORACLE_BAD_ARG;
+    double *x = (double *)malloc((size_t)V * sizeof(double));
+    double *top_x = (double *)malloc((size_t)k * sizeof(double));
+    int32_t *top_id = (int32_t *)malloc((size_t)k * sizeof(int32_t));
+    if (!x || !top_x || !top_id) {
+        free(x);
+        free(top_x);
+        free(top_id);
+        return ORACLE_BAD_ARG;
+    }
+    for (int row = 0; row < R; ++row) {
+        /* the product: one dot product per vocabulary row */
+        for (int v = 0; v < V; ++v) {
+            double dot = 0.0;
+            for (int h = 0; h < H; ++h)
+                dot += oracle_value(hidden, dtype, (size_t)row * H + h) *
+                       oracle_value(W_lm, dtype, (size_t)v * H + h);
+            x[v] = dot;
+            if (logits)
+                logits[(size_t)row * V + v] = dot;
+        }
+
+        double mx = -INFINITY;
+        for (int v = 0; v < V; ++v)
+            if (x[v] > mx)
+                mx = x[v];
+        double total = 0.0, carry = 0.0;
+        for (int v = 0; v < V; ++v) {
+            double t = exp(x[v] - mx);
+            double y = total + t;
+            if (fabs(total) >= fabs(t))
+                carry += (total - y) + t;
+            else
+                carry += (t - y) + total;
+            total = y;
+        }
+        const double x_lse = mx + log(total + carry);
+
+        int n = 0;
+        for (int v = 0; v < V; ++v) {
+            if (n == k && !comes_before(x[v], v, top_x[k - 1], top_id[k - 1]))
+                continue;
+            int pos = (n < k) ? n : k - 1;
+            while (pos > 0 && comes_before(x[v], v, top_x[pos - 1], top_id[pos - 1])) {
+                top_x[pos] = top_x[pos - 1];
+                top_id[pos] = top_id[pos - 1];
+                --pos;
+            }
+            top_x[pos] = x[v];
+            top_id[pos] = v;
+            if (n < k)
+                ++n;
+        }
+        for (int j = 0; j < k; ++j) {
+            cand_ids[(size_t)row * k + j] = top_id[j];
+            unary[(size_t)row * k + j] = top_x[j] - x_lse;
+        }
+        if (lse)
+            lse[row] = x_lse;
+    }
+    free(x);
+    free(top_x);
+    free(top_id);
+    return ORACLE_OK;
+}
+
+/*
  * Context gate: g[i][d] = sum_h hidden[i][h] * W_sel[h][d].
  * hidden: [R, H], W_sel: [H, r] (both act_dtype), g: [R, r].
  */

@@ -30,6 +30,12 @@ its logits, hidden rows and anchor; W_sel and the codebooks use the base seed):
   copied values (exact ties in the body).
 * Sums are formed in fp32 and rounded once to bf16 (round to nearest even) where the stored dtype
   is bf16. bf16 tensors are numpy ``uint16`` arrays of raw bits.
+
+The LM-head workloads (``LM_CONFIGS``: R rows of hidden state, an [V, H] LM-head weight, k) feed
+the fused LM-head top-k pass: W_lm ~ N(0, 9/H), so hidden ~ N(0, 1) rows give logits of spread
+about 3; each row then gets 8 distinct target tokens boosted by U[4, 8]: the row adds
+(boost / 9) * W_lm[target] (the target's squared norm is about 9), formed in fp32 before the one
+rounding to bf16.
 """
 from __future__ import annotations
 
@@ -46,6 +52,7 @@ LIBRARY = os.path.join(HERE, "libsynth.so")
 
 # stream ids (one per tensor role)
 S_LOGITS, S_BOOST_IDS, S_BOOST_VALS, S_HIDDEN, S_WSEL, S_PRED, S_SUCC, S_ANCHOR, S_TIES = range(1, 10)
+S_LM_W, S_LM_HIDDEN, S_LM_IDS, S_LM_BOOST = range(10, 14)
 
 
 def compile_synth(source: str = SOURCE, output: str = LIBRARY) -> str:
@@ -268,3 +275,37 @@ def from_torch(t) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
+
+
+# ---- LM-head workloads ------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class LmSpec:
+    name: str
+    R: int
+    H: int
+    V: int
+    k: int
+    seed: int
+
+
+LM_CONFIGS = {
+    "lmhead-qwen3-8b-b1": LmSpec("lmhead-qwen3-8b-b1", 16, 4096, 151936, 16, 6006),
+    "lmhead-serving-b64": LmSpec("lmhead-serving-b64", 1024, 4096, 151936, 16, 7007),
+}
+
+
+def lmhead_inputs(R: int, H: int, V: int, seed: int, targets: int = 8):
+    """hidden [R, H] and W_lm [V, H], both bf16 bits (see the module notes)."""
+    sw = 3.0 / np.sqrt(H)
+    W = normal(seed, S_LM_W, V * H, std=sw).reshape(V, H)
+    z = normal(seed, S_LM_HIDDEN, R * H).reshape(R, H)
+    m = min(targets, V)
+    if m > 0:
+        ids = distinct_ids(seed, S_LM_IDS, R, V, m)
+        val = uniform(seed, S_LM_BOOST, R * m, 4.0, 8.0).reshape(R, m)
+        scale = np.float32(1.0 / (H * sw * sw))
+        for i in range(R):
+            for j in range(m):
+                z[i] += (val[i, j] * scale) * W[ids[i, j]]
+    return to_bf16(z), to_bf16(W)

@@ -24,7 +24,10 @@ What pins what:
   * p_min stop: closed-form confidences 1 / (1 + e^-d) and the resulting block lengths, a
     confidence exactly at p_min, k = 1;
   * dynamic convolution: with a zero dynamic part, numpy's convolve per channel; the impulse
-    response (taps, the coefficient of the output row); block locality; the group broadcast.
+    response (taps, the coefficient of the output row); block locality; the group broadcast;
+  * LM-head top-k: the logits equal numpy's matmul of hidden with W_lm transposed, and the ids,
+    unary and lse equal a stable sort and scipy's logsumexp of those logits; one-hot W_lm rows
+    give logits x[i][v] = c_v * hidden[i][h(v)]; a zero hidden row gives lse = ln V.
 """
 from __future__ import annotations
 
@@ -549,6 +552,55 @@ def pin_conv_block_local_and_grouped(o):
     assert np.allclose(diff, want, rtol=1e-9, atol=1e-12), "group broadcast"
 
 
+# ---------------------------------------------------------------------- LM-head top-k
+
+def pin_lmhead_matmul_then_sort(o):
+    rng = np.random.default_rng(41)
+    for R, H, V, k, bf in [(3, 24, 50, 5, False), (4, 64, 700, 16, True), (1, 8, 16, 16, True)]:
+        h = rng.normal(0, 1, (R, H)).astype(np.float32)
+        w = (rng.normal(0, 3, (V, H)) / math.sqrt(H)).astype(np.float32)
+        if bf:
+            h = (h.view(np.uint32) & 0xFFFF0000).view(np.float32)
+            w = (w.view(np.uint32) & 0xFFFF0000).view(np.float32)
+            ids, unary, lse, x = o.lmhead_topk(bf16_bits(h), bf16_bits(w), k, want_logits=True)
+        else:
+            ids, unary, lse, x = o.lmhead_topk(h, w, k, want_logits=True)
+        want = h.astype(np.float64) @ w.astype(np.float64).T
+        scale = np.abs(h.astype(np.float64)) @ np.abs(w.astype(np.float64)).T
+        assert np.all(np.abs(x - want) <= 1e-13 * scale + 1e-300), "logits are hidden . W_lm^T"
+        for i in range(R):
+            order = sort_order(want[i])
+            assert np.array_equal(ids[i], order[:k])
+            want_lse = scipy.special.logsumexp(want[i])
+            assert abs(lse[i] - want_lse) <= 1e-12 * max(1.0, abs(want_lse))
+            assert np.allclose(unary[i], want[i][order[:k]] - want_lse, rtol=0, atol=1e-12)
+
+
+def pin_lmhead_onehot_weight(o):
+    rng = np.random.default_rng(42)
+    R, H, V, k = 5, 16, 40, 6
+    h = rng.normal(0, 1, (R, H)).astype(np.float32)
+    hv = rng.integers(0, H, V)
+    c = rng.choice([-2.0, -0.5, 0.25, 1.0, 3.0], V).astype(np.float32)
+    w = np.zeros((V, H), np.float32)
+    w[np.arange(V), hv] = c
+    ids, unary, lse, x = o.lmhead_topk(h, w, k, want_logits=True)
+    want = c[None, :].astype(np.float64) * h[:, hv].astype(np.float64)
+    assert np.array_equal(x, want), "vocabulary row v reads hidden column h(v) only"
+    for i in range(R):
+        assert np.array_equal(ids[i], sort_order(want[i])[:k])
+
+
+def pin_lmhead_zero_hidden(o):
+    rng = np.random.default_rng(43)
+    V, k = 97, 9
+    w = rng.normal(0, 1, (V, 32)).astype(np.float32)
+    ids, unary, lse = o.lmhead_topk(np.zeros((2, 32), np.float32), w, k)
+    assert np.array_equal(ids, np.tile(np.arange(k, dtype=np.int32), (2, 1)))
+    assert np.allclose(lse, math.log(V), rtol=0, atol=1e-13)
+    assert np.allclose(unary, -math.log(V), rtol=0, atol=1e-13)
+
+
 PINS = [
     pin_topk_full_sort, pin_topk_bruteforce_rank, pin_topk_boundary_ties, pin_topk_signed_zero,
     pin_topk_shift_invariance, pin_lse_normalises, pin_lse_scipy, pin_unary_softmax,
@@ -558,5 +610,6 @@ PINS = [
     pin_walk_score_and_margin, pin_walk_edge_tie, pin_reduces_to_argmax, pin_sample_frequencies,
     pin_sample_low_temperature_is_greedy, pin_sample_follows_predecessor, pin_pmin_closed_form,
     pin_sampled_confidence_and_margin, pin_conv_static_is_numpy_convolve, pin_conv_impulse,
-    pin_conv_block_local_and_grouped,
+    pin_conv_block_local_and_grouped, pin_lmhead_matmul_then_sort, pin_lmhead_onehot_weight,
+    pin_lmhead_zero_hidden,
 ]

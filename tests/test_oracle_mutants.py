@@ -48,6 +48,11 @@ MUTANTS = {
     "conv_group_index_modulo": [("* ng + c / G)", "* ng + c % ng)")],
     "conv_crosses_blocks": [("if (t - tap < 0)\n                        continue;", "if (b == 0 && t - tap < 0)\n                        continue;")],
     "conv_drops_base": [("oracle_value(base, dtype, (size_t)tap * C + c) +", "0.0 +")],
+    "lmhead_transposed_weight": [("oracle_value(W_lm, dtype, (size_t)v * H + h)", "oracle_value(W_lm, dtype, (size_t)h * V + v)")],
+    "lmhead_drops_first_h": [("for (int h = 0; h < H; ++h)\n                dot +=", "for (int h = 1; h < H; ++h)\n                dot +=")],
+    "lmhead_first_row_only": [("oracle_value(hidden, dtype, (size_t)row * H + h)", "oracle_value(hidden, dtype, (size_t)h)")],
+    "lmhead_unary_without_lse": [("top_x[j] - x_lse", "top_x[j]")],
+    "lmhead_lse_drops_max": [("const double x_lse = mx + log(total + carry);", "const double x_lse = log(total + carry);")],
 }
 
 
