@@ -15,8 +15,10 @@ Prints one JSON line:
                comes from committed rocprofv3 counter readings when they match the current kernel
   cpu_baseline the fp64 C oracle (single-threaded) on the host, on the same workload
   per_config   end-to-end latency and K1 bandwidth of every workload
-  extras       the default workload with the walk's sampling and p_min modes, and the grouped
-               dynamic depthwise convolution at the serving block shape
+  extras       the default workload with the walk's sampling and p_min modes, the grouped
+               dynamic depthwise convolution at the serving block shape, and the LM-head product
+               with the top-k pass folded in (16 rows, V = 151936, H = 4096), against its HBM
+               roofline, beside a library product followed by the top-k pass
 """
 from __future__ import annotations
 
@@ -204,6 +206,33 @@ def measure_dynconv(device: str, steps: int, warmup: int) -> dict:
             "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+def measure_lmhead(device: str, steps: int, warmup: int) -> dict:
+    """The LM-head product with the top-k pass folded into it (dflash2_lmhead_topk) at the
+    lmhead-qwen3-8b-b1 shape: 16 rows of hidden state, H = 4096, V = 151936, k = 16, bf16. Its
+    roofline is HBM: the [V, H] weight is read once. For context, the same result from a library
+    product that writes bf16 logits (torch.matmul) followed by the top-k pass."""
+    import torch
+    import dflash2_draft_candidate_amd as d2
+    import synth
+    s = synth.LM_CONFIGS["lmhead-qwen3-8b-b1"]
+    hb, wb = synth.lmhead_inputs(s.R, s.H, s.V, s.seed)
+    h, w = synth.as_torch(hb, device), synth.as_torch(wb, device)
+    del hb, wb
+    ms = time_loop(lambda i: d2.lmhead_topk(h, w, s.k), max(4, steps // 4), warmup)
+    nbytes = 2 * (s.V * s.H + s.R * s.H) + s.R * (8 * s.k + 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    ms_unfused = time_loop(lambda i: d2.topk_lse(torch.matmul(h, w.t()), s.k), max(4, steps // 4),
+                           warmup)
+    del h, w
+    torch.cuda.empty_cache()
+    return {"shape": {"workload": s.name, "R": s.R, "H": s.H, "V": s.V, "k": s.k,
+                      "dtype": "bf16"},
+            "us": round(ms * 1e3, 2), "algorithmic_bytes": nbytes, "gbs": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "tflops": round(2.0 * s.R * s.H * s.V / (ms * 1e-3) / 1e12, 1),
+            "unfused_matmul_plus_topk_us": round(ms_unfused * 1e3, 2)}
+
+
 def cpu_baseline(name: str, min_seconds: float = 12.0, max_passes: int = 64) -> dict:
     """The oracle (fp64 C, one thread) on the host over whole passes of the workload."""
     import oracle
@@ -381,7 +410,8 @@ def main():
     main_w = main_res.pop("_workload")
     s = main_w.s
     extras = {"walk_modes": measure_modes(main_w, args.steps, args.warmup),
-              "dynconv": measure_dynconv(device, args.steps, args.warmup)}
+              "dynconv": measure_dynconv(device, args.steps, args.warmup),
+              "lmhead_topk": measure_lmhead(device, args.steps, args.warmup)}
     log(f"[bench] extras: {extras}")
     del main_w
     log(f"[bench] {args.workload}: {main_res}")

@@ -29,6 +29,7 @@ F32, BF16 = 0, 1
 OK = 0
 MAX_K = 64
 MAX_R = 256
+LMHEAD_MAX_K = 16
 
 _vp, _ci, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 _lib.dflash2_version.restype = _ci
@@ -59,11 +60,16 @@ _lib.dflash2_select_ex.argtypes = [_vp, _ci, _vp, _ci, _vp, _vp, _vp, _ci, _vp] 
 _lib.dflash2_select_ex.restype = _ci
 _lib.dflash2_dynconv.argtypes = [_vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _vp]
 _lib.dflash2_dynconv.restype = _ci
+_lib.dflash2_lmhead_topk_workspace_bytes.argtypes = [_ci] * 4
+_lib.dflash2_lmhead_topk_workspace_bytes.restype = _sz
+_lib.dflash2_lmhead_topk.argtypes = [_vp, _vp] + [_ci] * 4 + [_vp, _vp, _vp, _vp, _sz, _vp]
+_lib.dflash2_lmhead_topk.restype = _ci
 
 EXPORTS = ("dflash2_version", "dflash2_status_string", "dflash2_workspace_bytes",
            "dflash2_select", "dflash2_topk_lse_workspace_bytes", "dflash2_topk_lse",
            "dflash2_gate_workspace_bytes", "dflash2_gate", "dflash2_lattice", "dflash2_walk",
-           "dflash2_select_ex", "dflash2_walk_ex", "dflash2_dynconv")
+           "dflash2_select_ex", "dflash2_walk_ex", "dflash2_dynconv",
+           "dflash2_lmhead_topk_workspace_bytes", "dflash2_lmhead_topk")
 
 
 class Dflash2Error(RuntimeError):
@@ -206,6 +212,28 @@ def topk_lse(logits: torch.Tensor, k: int):
     rc = _lib.dflash2_topk_lse(_ptr(logits), _dtype(logits), R, V, k, _ptr(ids), _ptr(unary),
                                _ptr(lse), _ptr(ws), ws.numel(), _stream(dev))
     _check(rc, "dflash2_topk_lse")
+    return ids, unary, lse
+
+
+def lmhead_topk(hidden: torch.Tensor, W_lm: torch.Tensor, k: int):
+    """hidden [R, H] bf16, W_lm [V, H] bf16 -> (cand_ids [R,k] int32, unary [R,k] f32, lse [R]
+    f32) of the top-k pass over hidden . W_lm^T, computed without materialising the logits."""
+    _contig(hidden, W_lm)
+    R, H = hidden.shape
+    V = W_lm.shape[0]
+    if W_lm.shape[1] != H or hidden.dtype != torch.bfloat16 or W_lm.dtype != torch.bfloat16:
+        raise ValueError("hidden [R, H] and W_lm [V, H], both bfloat16")
+    dev = hidden.device
+    ids = torch.empty((R, k), dtype=torch.int32, device=dev)
+    unary = torch.empty((R, k), dtype=torch.float32, device=dev)
+    lse = torch.empty((R,), dtype=torch.float32, device=dev)
+    need = _lib.dflash2_lmhead_topk_workspace_bytes(R, H, V, k)
+    if need == 0:
+        raise Dflash2Error(-1, "dflash2_lmhead_topk: unsupported sizes")
+    ws = _workspace(need, dev)
+    rc = _lib.dflash2_lmhead_topk(_ptr(hidden), _ptr(W_lm), R, H, V, k, _ptr(ids), _ptr(unary),
+                                  _ptr(lse), _ptr(ws), ws.numel(), _stream(dev))
+    _check(rc, "dflash2_lmhead_topk")
     return ids, unary, lse
 
 

@@ -174,6 +174,27 @@ int dflash2_dynconv(const void *x, const void *base, const void *dyn, int dtype,
                                      static_cast<hipStream_t>(stream)));
 }
 
+size_t dflash2_lmhead_topk_workspace_bytes(int R, int H, int V, int k) {
+    if (R < 1 || H < 8 || H % 8 != 0 || V < 1 || V > DFLASH2_MAX_V || k < 1 ||
+        k > DFLASH2_LMHEAD_MAX_K || k > lmhead_max_k() || k > V)
+        return 0;
+    return lmhead_workspace_bytes(R, V);
+}
+
+int dflash2_lmhead_topk(const void *hidden, const void *W_lm, int R, int H, int V, int k,
+                        int32_t *cand_ids, float *unary, float *lse, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    const size_t need = dflash2_lmhead_topk_workspace_bytes(R, H, V, k);
+    if (need == 0) return DFLASH2_ERR_INVALID_ARG;
+    int rc = check_ptrs({hidden, W_lm, cand_ids, unary});
+    if (rc) return rc;
+    if (lse && !aligned16(lse)) return DFLASH2_ERR_ALIGNMENT;
+    if (!workspace || workspace_bytes < need) return DFLASH2_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return DFLASH2_ERR_ALIGNMENT;
+    return hip_status(launch_lmhead_topk(hidden, W_lm, R, H, V, k, cand_ids, unary, lse,
+                                         workspace, static_cast<hipStream_t>(stream)));
+}
+
 size_t dflash2_workspace_bytes(int B, int L, int V, int H, int r, int k) {
     if (B < 1 || L < 1 || H < 1 || r < 1 || r > DFLASH2_MAX_R || rows_of(B, L) > INT_MAX ||
         check_rows((int)rows_of(B, L), V, k) != DFLASH2_OK)

@@ -71,6 +71,15 @@ hipError_t launch_walk(const float *edges, const int32_t *cand_ids, int B, int L
                        int32_t *path, int32_t *path_idx, hipStream_t stream,
                        const WalkMode *mode = nullptr);
 
+// ---- LM-head product with the top-k pass in its epilogue -------------------------------------
+// hidden [R, H] and W_lm [V, H] bf16 (H % 8 == 0), k <= lmhead_max_k(); workspace:
+// lmhead_workspace_bytes(R, V) bytes of range partials.
+int lmhead_max_k();
+size_t lmhead_workspace_bytes(int R, int V);
+hipError_t launch_lmhead_topk(const void *hidden, const void *W_lm, int R, int H, int V, int k,
+                              int32_t *cand_ids, float *unary, float *lse, void *workspace,
+                              hipStream_t stream);
+
 // ---- grouped dynamic depthwise convolution of the draft blocks ------------------------------
 hipError_t launch_dynconv(const void *x, const void *base, const void *dyn, int dtype, int nb,
                           int Tn, int C, int K, int G, void *y, hipStream_t stream);

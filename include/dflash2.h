@@ -43,11 +43,12 @@
 extern "C" {
 #endif
 
-#define DFLASH2_ABI_VERSION 2
+#define DFLASH2_ABI_VERSION 3
 #define DFLASH2_MAX_K 64  /* largest top-k */
 #define DFLASH2_MAX_R 256 /* largest codebook rank r */
 #define DFLASH2_MAX_V (1 << 28) /* largest vocabulary (a row's bytes stay within 32-bit offsets) */
 #define DFLASH2_MAX_CONV_TAPS 8 /* largest kernel of dflash2_dynconv */
+#define DFLASH2_LMHEAD_MAX_K 16 /* largest k of dflash2_lmhead_topk */
 
 typedef enum dflash2_dtype {
     DFLASH2_F32 = 0,  /* IEEE binary32 */
@@ -215,6 +216,31 @@ int dflash2_walk_ex(const float *edges, const int32_t *cand_ids, int B, int L, i
  */
 int dflash2_dynconv(const void *x, const void *base, const void *dyn, int dtype, int n_blocks,
                     int T, int C, int K, int group, void *y, void *stream);
+
+/*
+ * dflash2_lmhead_topk - the drafter's LM-head product with the top-k pass folded into it: the
+ *   [R, V] logits exist only in registers. Sources: "DFlash2 Lands in llama.cpp" (ramgpt.org),
+ *   section "What llama.cpp Actually Builds for the Selector" (the per-position top-k over the
+ *   logits of the drafter's full-vocabulary projection) and section "The Most Important
+ *   Performance Question Is Now Different" (top-k extraction is one of the draft cycle's costs).
+ *   The fusion is this library's design.
+ *
+ *   hidden   [R, H]  bf16, device, row-major. The drafter's final hidden states.
+ *   W_lm     [V, H]  bf16, device, row-major. The LM-head weight (one row per vocabulary token).
+ *   x[i][v] = sum_h hidden[i][h] * W_lm[v][h] (bf16 products, fp32 accumulation); then, as
+ *   dflash2_topk_lse over x:
+ *   cand_ids [R, k]  int32, device, out. The first k tokens of the candidate order.
+ *   unary    [R, k]  fp32, device, out. x[i][cand_j] - lse_i.
+ *   lse      [R]     fp32, device, out, may be NULL. logsumexp_v x[i][v].
+ *   R >= 1; H >= 8 and H % 8 == 0; 1 <= V <= DFLASH2_MAX_V; 1 <= k <= min(V, DFLASH2_LMHEAD_MAX_K).
+ * Workspace: dflash2_lmhead_topk_workspace_bytes(R, H, V, k) bytes (range partials), 16-byte
+ * aligned, owned by the caller; contents need not be initialised. Errors: DFLASH2_ERR_INVALID_ARG,
+ * DFLASH2_ERR_ALIGNMENT (every pointer 16-byte aligned), DFLASH2_ERR_WORKSPACE, DFLASH2_ERR_HIP.
+ */
+size_t dflash2_lmhead_topk_workspace_bytes(int R, int H, int V, int k);
+int dflash2_lmhead_topk(const void *hidden, const void *W_lm, int R, int H, int V, int k,
+                        int32_t *cand_ids, float *unary, float *lse, void *workspace,
+                        size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -43,6 +43,9 @@ def lib():
     L.dflash2_select_ex.argtypes = [vp, ci, vp, ci, vp, vp, vp, ci, vp] + [ci] * 6 + \
         [cf, vp, cf, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dflash2_dynconv.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, vp, vp]
+    L.dflash2_lmhead_topk.argtypes = [vp, vp] + [ci] * 4 + [vp, vp, vp, vp, sz, vp]
+    L.dflash2_lmhead_topk_workspace_bytes.argtypes = [ci] * 4
+    L.dflash2_lmhead_topk_workspace_bytes.restype = sz
     L.dflash2_status_string.argtypes = [ci]
     L.dflash2_status_string.restype = ctypes.c_char_p
     return L
@@ -58,7 +61,8 @@ def test_header_declares_the_abi():
     names = declared_functions()
     for f in ("dflash2_select", "dflash2_workspace_bytes", "dflash2_status_string",
               "dflash2_topk_lse", "dflash2_gate", "dflash2_lattice", "dflash2_walk",
-              "dflash2_select_ex", "dflash2_walk_ex", "dflash2_dynconv"):
+              "dflash2_select_ex", "dflash2_walk_ex", "dflash2_dynconv", "dflash2_lmhead_topk",
+              "dflash2_lmhead_topk_workspace_bytes"):
         assert f in names
 
 
@@ -70,7 +74,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_binding_covers_the_abi():
     import dflash2_draft_candidate_amd as d2
     assert sorted(d2.EXPORTS) == declared_functions()
-    assert d2.version() == 2
+    assert d2.version() == 3
 
 
 def test_status_strings(lib):
@@ -163,6 +167,25 @@ def test_dynconv_rejects(lib, kw, status):
     a.update(kw)
     assert lib.dflash2_dynconv(a["x"], a["base"], a["dyn"], a["dt"], a["nb"], a["T"], a["C"],
                                a["K"], a["G"], a["y"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), EINVAL), (dict(k=17), EINVAL), (dict(k=101), EINVAL), (dict(H=12), EINVAL),
+    (dict(H=0), EINVAL), (dict(R=0), EINVAL), (dict(V=0), EINVAL), (dict(hidden=None), EINVAL),
+    (dict(W=None), EINVAL), (dict(ids=None), EINVAL), (dict(W=MIS), EALIGN),
+    (dict(lse=MIS), EALIGN), (dict(ws=None), EWS), (dict(wsb=16), EWS), (dict(ws=MIS), EALIGN),
+])
+def test_lmhead_rejects(lib, kw, status):
+    a = dict(hidden=P, W=P, R=16, H=64, V=100, k=16, ids=P, un=P, lse=None, ws=P, wsb=1 << 30)
+    a.update(kw)
+    assert lib.dflash2_lmhead_topk(a["hidden"], a["W"], a["R"], a["H"], a["V"], a["k"], a["ids"],
+                                   a["un"], a["lse"], a["ws"], a["wsb"], None) == status
+
+
+def test_lmhead_workspace_sizes(lib):
+    assert lib.dflash2_lmhead_topk_workspace_bytes(16, 4096, 151936, 16) > 0
+    assert lib.dflash2_lmhead_topk_workspace_bytes(16, 4096, 151936, 17) == 0
+    assert lib.dflash2_lmhead_topk_workspace_bytes(16, 4100, 151936, 16) == 0
 
 
 def test_binding_rejects_host_tensors():
