@@ -11,10 +11,11 @@
 // is one of the draft cycle's costs). Folding the top-k into the projection is this library's
 // design: it removes the [R, V] logits round trip through HBM.
 //
-// Design (gfx950, wave64; four waves per workgroup, no LDS staging of operands):
+// Design (gfx950, wave64; four waves per workgroup, no LDS staging of operands; RT = 1 row tile
+// of 16 for R <= 16, 2 for R <= 64, else 4):
 //   * Work. A workgroup takes a block of 16 * RT rows and a contiguous range of the vocabulary;
 //     its four waves split the range into contiguous runs of 16-column tiles, and a wave handles
-//     up to four tiles per pass over H. Workgroups number their row blocks XCD by XCD, so the row
+//     its run in passes over H of equal size (at most four tiles). Workgroups number their row blocks XCD by XCD, so the row
 //     blocks that read one vocabulary range share its W_lm lines in one L2.
 //   * Product. v_mfma_f32_16x16x32_bf16 with fp32 accumulation. Both operands are K-contiguous
 //     (rows of hidden for A, rows of W_lm for B): per step of 64 h a lane loads 16 consecutive
@@ -252,7 +253,11 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_topk_kernel(LmJob job) {
         }
 
     const int ns = (H + 63) / 64;  // steps over H (two MFMAs each)
-    for (int tc = tc0; tc < tc1; tc += kLmGroup) {
+    // passes of equal size (at most kLmGroup tiles): no pass much smaller than the others
+    const int npass = (tc1 - tc0 + kLmGroup - 1) / kLmGroup;
+    const int per = npass > 0 ? (tc1 - tc0 + npass - 1) / npass : kLmGroup;
+    for (int tc = tc0; tc < tc1; tc += per) {
+        const int te = min(tc + per, tc1);  // this pass: tiles tc .. te - 1
         const uint16_t *brow[kLmGroup];
 #pragma unroll
         for (int c = 0; c < kLmGroup; ++c)
@@ -267,7 +272,7 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_topk_kernel(LmJob job) {
         // row (32 bytes: four groups cover a 128-byte line), and the two MFMAs of the step take
         // the first and the second 8 as their K slots 8 g .. 8 g + 7 (the same map for both
         // operands, so the sum over h is unchanged). Tiles past the wave's run load nothing.
-        const int live = min(kLmGroup, tc1 - tc);
+        const int live = te - tc;
         u32x4 fa[D][RT][2], fb[D][kLmGroup][2];
         auto load = [&](int d, int s) {
             const int kc = 64 * s + 16 * g;
@@ -318,7 +323,7 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_topk_kernel(LmJob job) {
 #pragma unroll
                 for (int c = 0; c < kLmGroup; ++c) {
                     const int col = (tc + c) * 16 + m;
-                    const bool ok = tc + c < tc1 && col < V;
+                    const bool ok = tc + c < te && col < V;
                     const float x = acc[rt][c][i];
                     key[c] = ok ? cand_key(x, col) : 0ull;
                     xl[c] = ok ? x * kLog2e : -INFINITY;
@@ -430,7 +435,7 @@ struct LmPlan {
 
 LmPlan plan_lmhead(int R, int V) {
     LmPlan p;
-    p.RT = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
+    p.RT = R <= 16 ? 1 : (R <= 64 ? 2 : 4);
     p.rblocks = (R + 16 * p.RT - 1) / (16 * p.RT);
     p.col16 = (V + 15) / 16;
     int ranges = kLmTargetWgs / p.rblocks;

@@ -87,12 +87,12 @@ def check_rows(gpu, want, hidden, W, k, rows=None):
 CASES = [
     # R, H, V, k, seed
     (5, 64, 300, 4, 1),
-    (37, 200, 1111, 16, 2),     # ragged rows (row blocks of 64), H not a multiple of 32, ragged V
+    (37, 200, 1111, 16, 2),     # ragged rows (row blocks of 32), H not a multiple of 32, ragged V
     (16, 1024, 20011, 16, 3),
     (20, 128, 16, 16, 4),       # V = k: one 16-column tile, most waves without a tile
     (1, 8, 100, 1, 5),          # one row, one step, k = 1
     (130, 256, 3000, 8, 6),     # three row blocks of 64
-    (33, 96, 4099, 16, 7),      # two row blocks of 32
+    (70, 96, 4099, 16, 7),      # two row blocks of 64 (ragged)
 ]
 
 
