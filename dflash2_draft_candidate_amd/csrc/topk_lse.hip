@@ -25,16 +25,20 @@
 //     sends the unit down a slow exact path at the end.
 //   * top-k. A 64-bit key (order-preserving logit map above the inverted id) makes the candidate
 //     order one unsigned compare. The unit's oldest wave (its owner) keeps the unit's 64 best
-//     keys sorted across its lanes; the other waves queue their candidates to it through LDS
-//     (a wave that finds the queue full keeps them in a list of its own, merged at the end). An
+//     keys sorted across its lanes; the other waves queue their candidates to it through LDS,
+//     the survivors of one staged lane in consecutive slots reserved with one atomic (a wave
+//     that finds the queue full keeps them in a list of its own, merged at the end). An
 //     element is admitted only if it beats the unit's threshold in LDS, which is always valid
-//     (k real elements at or above it): the k-th key of a wave's list, or the seed below. A batch costs
-//     one compare per lane of the lane's term sum unless it reaches the threshold's term; then
-//     each such lane's batch is staged in LDS and read back transposed (lane j <- element j),
-//     and each surviving candidate is inserted by ballot + popcount rank and a one-lane DPP
-//     shift.
+//     (k real elements at or above it): the k-th key of a wave's list, or the seed below. A
+//     batch costs one compare per lane of the lane's term sum unless it reaches the threshold's
+//     term; then each such lane's batch is staged in LDS and read back transposed (lane j <-
+//     element j), and the owner inserts each surviving candidate by ballot + popcount rank and
+//     a one-lane DPP shift. After its stream the owner takes what is queued 64 at a time and,
+//     when more than a few pass the threshold, sorts them and merges the two sorted lists.
 //   * Seed. The threshold starts at the k-th largest of the lane maxima of the unit's waves over
-//     their first batches (k real elements reach it).
+//     their first batches (k real elements reach it); with more than four waves per unit, the
+//     k-th largest of the lane-wise maxima over the waves (one search instead of one per
+//     wave, so small units get it before most of their batches are read).
 //   * End. The owner keeps draining the queue until every wave of its unit has finished the
 //     stream; after a barrier each wave adds a fixed range of the unit's chunk sums, and the
 //     owner merges any kept lists (bitonic merge: the top k of distinct keys is unique), adds the
@@ -59,7 +63,7 @@ constexpr int kWaves = 16;                // waves per workgroup: one workgroup 
 constexpr int kThreads = kWaves * kWave;
 constexpr int kMaxUnits = 8;              // units per workgroup (W = kWaves / G >= 2)
 constexpr int kTargetWorkgroups = 256;    // one per CU
-constexpr int kMinBatchesPerWave = 2;     // slices are not cut smaller than this per wave
+constexpr int kMinBatchesPerWave = 1;     // slices are not cut smaller than this per wave
 constexpr size_t kLdsBudget = 120 * 1024; // dynamic LDS (chunk sums, gate tiles) per workgroup
 constexpr float kSumLimit = 0x1p100f;     // a chunk sum above this leaves the fast path
 constexpr float kSumFloor = 0x1p-60f;     // so does a unit total below this
@@ -108,6 +112,7 @@ struct K1Shared {
     u32x4 stage[kWaves][kU];          // per wave: one hit lane's batch, read back transposed
     uint32_t next_chunk[kMaxUnits];   // next chunk of the unit to hand out
     uint32_t seeded[kMaxUnits];       // waves of the unit that have published their seed
+    uint32_t seed_done[kMaxUnits];    // the unit's seed is in tau
     uint32_t overflow[kMaxUnits];     // a chunk sum left the safe range
     uint32_t gate_arrived;            // gate waves that have stored their part of the tile
     int64_t unit_c0[kMaxUnits];       // each unit's first whole vector,
@@ -224,15 +229,16 @@ __device__ __forceinline__ void wave_insert(WaveTopk &w, uint64_t c, int lane) {
     raise_tau(w, lane_value(w.top, w.k - 1), lane);
 }
 
-// Reserve the next queue slot if the queue has room (its previous occupant consumed).
-__device__ __forceinline__ bool try_reserve(WaveTopk &w, int lane, uint32_t &pos) {
+// Reserve n consecutive queue slots if the queue has room for them (their previous occupants
+// consumed).
+__device__ __forceinline__ bool try_reserve(WaveTopk &w, int lane, uint32_t n, uint32_t &pos) {
     uint32_t ok = 0u, p = 0u;
     if (lane == 0) {
         const uint32_t head =
             __hip_atomic_load(w.q_head, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
         uint32_t tail = __hip_atomic_load(w.q_tail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        while (tail - head <= w.qmask) {
-            if (__hip_atomic_compare_exchange_strong(w.q_tail, &tail, tail + 1u, __ATOMIC_RELAXED,
+        while (tail + n - head <= w.qmask + 1u) {
+            if (__hip_atomic_compare_exchange_strong(w.q_tail, &tail, tail + n, __ATOMIC_RELAXED,
                                                      __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_WORKGROUP)) {
                 ok = 1u;
@@ -245,35 +251,63 @@ __device__ __forceinline__ bool try_reserve(WaveTopk &w, int lane, uint32_t &pos
     return __builtin_amdgcn_readfirstlane(ok) != 0u;
 }
 
-// A candidate above the threshold: the owner inserts it; another wave queues it for the owner.
-// If the queue is full, a wave of the unit keeps it in its own list (merged at the end), and a
-// wave helping from another unit waits for room (the owner drains until every wave is done).
-// A reserved slot is written at once, so the queue never holds a hole.
-__device__ __forceinline__ void accept(WaveTopk &w, uint64_t c, int lane) {
-    if (w.owner) {
-        wave_insert(w, c, lane);
+// Candidates above which a set is sorted and merged into the list in one go instead of being
+// inserted one at a time (a bitonic sort and merge cost about as much as this many inserts).
+constexpr int kBulkInsert = 6;
+
+// Add the candidates c (one per lane, 0 = none; every nonzero one above the threshold) to the
+// wave's list: one insert at a time, or (BULK, for many) sort them and merge the two sorted
+// lists (the 64 largest keys of both; keys are distinct, so the result is the same either
+// way). The sort holds too many registers for the stream loop, so only the owner's drain after
+// the stream uses it.
+template <bool BULK>
+__device__ __forceinline__ void insert_set(WaveTopk &w, uint64_t c, int lane) {
+    uint64_t m = __ballot(c != 0ull);
+    if (BULK && __popcll(m) > kBulkInsert) {
+        w.top = wave_merge_desc(w.top, wave_sort_desc(c, lane), lane);
+        raise_tau(w, lane_value(w.top, w.k - 1), lane);
         return;
     }
+    while (m != 0ull) {
+        const int src = __builtin_ctzll(m);
+        m &= m - 1ull;
+        const uint64_t cs = lane_value(c, src);
+        if (cs > w.tau_key) wave_insert(w, cs, lane);
+    }
+}
+
+// A non-owner's candidates: lanes in m, lane j holding logit x with id `id0 + j_offset(j)`.
+// They go to the owner's queue in consecutive slots reserved at once (each lane builds its own
+// key only for the store); true once queued. If the queue has no room, a wave of the unit gets
+// false and keeps them in its own list (merged at the end), and a wave helping from another
+// unit waits for room (the owner drains until every wave is done). Reserved slots are written
+// at once, so the queue never holds a hole for long. Keys at or below the threshold may be
+// queued; the owner drops them.
+template <int EV>
+__device__ __forceinline__ bool queue_set(WaveTopk &w, uint64_t m, float x, int32_t id0,
+                                          int lane) {
+    const uint32_t n = (uint32_t)__popcll(m);
     for (;;) {
         uint32_t pos;
-        if (try_reserve(w, lane, pos)) {
-            if (lane == 0)
-                __hip_atomic_store(&w.queue[pos & w.qmask], c, __ATOMIC_RELEASE,
-                                   __HIP_MEMORY_SCOPE_WORKGROUP);
-            return;
+        if (try_reserve(w, lane, n, pos)) {
+            if ((m >> lane) & 1ull) {
+                const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
+                    (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                const int32_t id = id0 + (lane / EV) * kWave * EV + (lane % EV);
+                __hip_atomic_store(&w.queue[(pos + rank) & w.qmask], cand_key(x, id),
+                                   __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+            return true;
         }
-        if (w.home) {
-            wave_insert(w, c, lane);
-            w.spilled = true;
-            return;
-        }
+        if (w.home) return false;
         __builtin_amdgcn_s_sleep(1);
     }
 }
 
 // Owner: insert the queued candidates, consuming the written prefix of the queue (a reserved
 // slot not yet written stops it until the next call). `all`: after the stream, when every
-// reserved slot is written: take them all.
+// reserved slot is written: take them all. BULK: sort and merge large sets (see insert_set).
+template <bool BULK>
 __device__ __forceinline__ void drain(WaveTopk &w, int lane, bool all) {
     const uint32_t tail = __builtin_amdgcn_readfirstlane(
         __hip_atomic_load(w.q_tail, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
@@ -290,13 +324,7 @@ __device__ __forceinline__ void drain(WaveTopk &w, int lane, bool all) {
             cnt = gaps ? (uint32_t)__builtin_ctzll(gaps) : n;
         }
         if (cnt == 0u) return;
-        uint64_t m = written & (cnt >= 64 ? ~0ull : ((1ull << cnt) - 1ull));
-        while (m != 0ull) {
-            const int src = __builtin_ctzll(m);
-            m &= m - 1ull;
-            const uint64_t c = lane_value(key, src);
-            if (c > w.tau_key) wave_insert(w, c, lane);
-        }
+        insert_set<BULK>(w, lane < (int)cnt && key > w.tau_key ? key : 0ull, lane);
         if (lane < (int)cnt)
             __hip_atomic_store(&w.queue[slot], 0ull, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -333,14 +361,19 @@ __device__ __forceinline__ void offer_lanes(WaveTopk &w, const u32x4 *buf, uint6
         if (j < NSLOT) x = Elem<T>::lds_element(stage, j);
         const bool maybe = j < NSLOT && vec_j + L < nvalid && x >= w.tau_v && x != -INFINITY;
         uint64_t m = __ballot(maybe);
+        if (m == 0ull) continue;
+        const int32_t id0 = id_base + L * lane_stride;
+        if (!w.owner) {
+            if (queue_set<EV>(w, m, x, id0, lane)) continue;
+            w.spilled = true;  // the queue was full: this wave keeps them
+        }
         while (m != 0ull) {
-            // each candidate's key is built from wave-uniform values (scalar unit)
+            // inserted one by one; each key is built from wave-uniform values
             const int src = __builtin_ctzll(m);
             m &= m - 1ull;
             const float xs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), src));
-            const int32_t id = id_base + L * lane_stride + (src / EV) * kWave * EV + (src % EV);
-            const uint64_t c = cand_key(xs, id);
-            if (c > w.tau_key) accept(w, c, lane);
+            const uint64_t c = cand_key(xs, id0 + (src / EV) * kWave * EV + (src % EV));
+            if (c > w.tau_key) wave_insert(w, c, lane);
         }
     }
 }
@@ -419,17 +452,23 @@ struct UnitRange {
     int64_t t0, t1;  // ragged tail [t0, t1)
 };
 
+// floor(n * s / S) for n < 2^31 and s <= S < 2^16, in 32-bit arithmetic (n = a S + b gives
+// a s + floor(b s / S)); 64-bit divisions cost hundreds of scalar instructions.
+__device__ __forceinline__ int64_t split_point(uint32_t n, uint32_t s, uint32_t S) {
+    return (int64_t)(n / S) * s + (n % S) * s / S;
+}
+
 __device__ __forceinline__ UnitRange unit_range(int64_t unit, int V, int S, int EV) {
     UnitRange u;
-    const int64_t row = unit / S;
-    const int slice = (int)(unit % S);
-    u.g0 = row * (int64_t)V;
+    const uint32_t row = (uint32_t)unit / (uint32_t)S;  // units and slices fit in 31 bits
+    const uint32_t slice = (uint32_t)unit - row * (uint32_t)S;
+    u.g0 = (int64_t)row * V;
     const int64_t g1 = u.g0 + V;
     int64_t va = (u.g0 + EV - 1) / EV, vb = g1 / EV;
     if (va > vb) va = vb = 0;  // the row lies inside one vector: all of it is ragged
-    const int64_t nvec = vb - va;
-    u.c0 = va + nvec * slice / S;
-    u.nv = (int)(va + nvec * (slice + 1) / S - u.c0);
+    const uint32_t nvec = (uint32_t)(vb - va);
+    u.c0 = va + split_point(nvec, slice, (uint32_t)S);
+    u.nv = (int)(va + split_point(nvec, slice + 1, (uint32_t)S) - u.c0);
     u.h0 = u.h1 = u.t0 = u.t1 = 0;
     if (slice == 0) {
         u.h0 = u.g0;
@@ -524,7 +563,7 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     if (threadIdx.x < kMaxUnits) sh.q_tail[threadIdx.x] = sh.q_head[threadIdx.x] = 0u;
     if (threadIdx.x == 0) sh.spilled = 0u;
     for (int i = threadIdx.x; i < kQueueSlots; i += kThreads) sh.queue[i] = 0ull;
-    if (threadIdx.x < kMaxUnits) sh.seeded[threadIdx.x] = 0u;
+    if (threadIdx.x < kMaxUnits) sh.seeded[threadIdx.x] = sh.seed_done[threadIdx.x] = 0u;
     if (threadIdx.x == 0) sh.gate_arrived = sh.done_all = 0u;
     if (wv == 0 && lane == 0) {
         sh.unit_c0[q] = ur.c0;
@@ -671,11 +710,19 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     w.home = true;
     w.spilled = false;
     set_tau(w, 0ull);
-    // Threshold seed, with no barrier: the wave starts from the k-th largest of its own 64 lane
-    // maxima, then publishes them; the unit's last wave to publish raises the unit threshold to
-    // the k-th largest of all of them. Either has k real elements at or above it. The k-th
-    // largest of a set of order-preserving value keys is the largest t with at least k keys at
-    // or above it, found one bit at a time from the top with ballot counts.
+    // Threshold seed: the wave starts from the k-th largest of its own 64 lane maxima, then
+    // publishes them; the unit's last wave to publish raises the unit threshold to the k-th
+    // largest of all of them. Either has k real elements at or above it. The k-th largest of a
+    // set of order-preserving value keys is the largest t with at least k keys at or above it,
+    // found one bit at a time from the top with ballot counts. The gate waves (which reach this
+    // point only after their tile) do not take part. A unit whose batches the first ones of its
+    // waves nearly cover waits for the unit threshold before it offers anything (a short wait
+    // that spares the owner most of the candidates); a longer unit does not wait, nor does one
+    // with at most one batch per wave (the threshold would come after every batch is read).
+    const bool has_tile = NTG > 0 && xcd_major(blockIdx.x, gridDim.x) < gj.mtiles * gj.splits;
+    auto gate_slot = [&](int s) {
+        return has_tile && s >= gate_first_wave<G>() && s < gate_first_wave<G>() + kGateWaves;
+    };
     if (active) {
         const uint32_t mk = sh.seed_vals[wave * kWave + lane];
         uint32_t t = 0u;
@@ -684,24 +731,61 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
             if (__popcll(__ballot(mk >= c)) >= k) t = c;
         }
         raise_tau(w, (uint64_t)t << 32, lane);
-        uint32_t arrived = 0u;
-        if (lane == 0)
-            arrived = __hip_atomic_fetch_add(&sh.seeded[q], 1u, __ATOMIC_ACQ_REL,
-                                             __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (__builtin_amdgcn_readfirstlane(arrived) == W - 1) {
-            // the last of the unit to arrive: every peer's maxima are in LDS
-            uint32_t v[W];
+        int n_seed = 0;  // the unit's waves that are not gate waves (at least its owner)
 #pragma unroll
-            for (int i = 0; i < W; ++i) v[i] = sh.seed_vals[unit_slot<G>(q, i) * kWave + lane];
-            uint32_t u = 0u;
-            for (int bit = 31; bit >= 0; --bit) {
-                const uint32_t c = u | (1u << bit);
-                int n = 0;
+        for (int i = 0; i < W; ++i) n_seed += gate_slot(unit_slot<G>(q, i)) ? 0 : 1;
+        const bool wait_seed = nb > W && nb <= W * kSeedBatches;
+        if (!gate_slot(wave)) {
+            uint32_t arrived = 0u;
+            if (lane == 0)
+                arrived = __hip_atomic_fetch_add(&sh.seeded[q], 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (__builtin_amdgcn_readfirstlane(arrived) == (uint32_t)n_seed - 1u) {
+                // the last to arrive: every other seeding wave's maxima are in LDS. Up to four
+                // waves: the k-th largest of all their maxima. More: the k-th largest of the 64
+                // lane-wise maxima over the waves (each is a real element of a lane position no
+                // other shares, so k of them at or above it are k real elements), one search
+                // instead of one per wave.
+                uint32_t u = 0u;
+                if constexpr (W <= 4) {
+                    uint32_t v[W];
 #pragma unroll
-                for (int i = 0; i < W; ++i) n += __popcll(__ballot(v[i] >= c));
-                if (n >= k) u = c;
+                    for (int i = 0; i < W; ++i) {
+                        const int si = unit_slot<G>(q, i);
+                        v[i] = gate_slot(si) ? 0u : sh.seed_vals[si * kWave + lane];
+                    }
+                    for (int bit = 31; bit >= 0; --bit) {
+                        const uint32_t c = u | (1u << bit);
+                        int n = 0;
+#pragma unroll
+                        for (int i = 0; i < W; ++i) n += __popcll(__ballot(v[i] >= c));
+                        if (n >= k) u = c;
+                    }
+                } else {
+                    uint32_t v = 0u;
+#pragma unroll
+                    for (int i = 0; i < W; ++i) {
+                        const int si = unit_slot<G>(q, i);
+                        const uint32_t sv = gate_slot(si) ? 0u : sh.seed_vals[si * kWave + lane];
+                        v = sv > v ? sv : v;
+                    }
+                    for (int bit = 31; bit >= 0; --bit) {
+                        const uint32_t c = u | (1u << bit);
+                        if (__popcll(__ballot(v >= c)) >= k) u = c;
+                    }
+                }
+                raise_tau(w, (uint64_t)u << 32, lane);
+                if (lane == 0)
+                    __hip_atomic_store(&sh.seed_done[q], 1u, __ATOMIC_RELEASE,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
             }
-            raise_tau(w, (uint64_t)u << 32, lane);
+            if (wait_seed) {  // every seeding wave gets here without waiting on anything
+                while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                           &sh.seed_done[q], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) ==
+                       0u)
+                    __builtin_amdgcn_s_sleep(1);
+                pull_tau(w);
+            }
         }
     }
     // logsumexp reference, fixed for every unit: terms are 2^(x log2e). Rows whose terms leave
@@ -757,7 +841,7 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
                 set_tau(w, 0ull);
                 te_key = ~0ull;
             }
-            if (w.owner) drain(w, lane, false);
+            if (w.owner) drain<false>(w, lane, false);
             pull_tau(w);
             if (w.tau_key != te_key) {  // the threshold's term, recomputed only when it moved
                 te_key = w.tau_key;
@@ -788,7 +872,7 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
         while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
                    &sh.done_all, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) <
                (uint32_t)kWaves) {
-            drain(w, lane, false);
+            drain<true>(w, lane, false);
             __builtin_amdgcn_s_sleep(2);
         }
     }
@@ -820,7 +904,7 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     }
     __syncthreads();
     if (!rag_owner) return;
-    drain(w, lane, true);
+    drain<true>(w, lane, true);
     uint32_t sp = sh.spilled & peers;
     while (sp != 0u) {
         const int s = __builtin_ctz(sp);
