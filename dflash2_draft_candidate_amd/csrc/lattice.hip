@@ -52,6 +52,9 @@ constexpr int kLatWaves = 16;                 // waves per workgroup at most
 constexpr int lat_waves(int kt, int cb) { return kt == 4 || (kt == 2 && cb == 4) ? 8 : kLatWaves; }
 constexpr int kRankChunk = 64;                // ranks per chunk: 4 lane groups x 16 steps
 constexpr int kMaxPasses = 4;                 // the walk rides along up to this many passes
+constexpr int kMaxSplit = 8;                  // gate partials per row at most (split-K)
+template <typename CB, int KT>
+constexpr bool kPipelined = sizeof(CB) == 2 && KT == 1;  // codebook chunks loaded one ahead
 
 // 16 consecutive codebook values of one row as raw 16-byte vectors.
 template <typename CB>
@@ -83,21 +86,31 @@ __device__ __forceinline__ void widen(const Seg<CB> &s, float *x) {
     for (int q = 0; q < Seg<CB>::NV; ++q) Elem<CB>::unpack(s.v[q], x + q * Seg<CB>::EV);
 }
 
-// The gate value at offset `off` of each of the ksplit partial rows (stride apart), added in split
-// order from 0; N loads in flight at a time (clamped indices: no branch between the loads).
-template <int N>
-__device__ __forceinline__ float sum_parts(const float *gpart, int ksplit, int64_t stride,
-                                           int64_t off) {
-    float v = 0.f;
-    for (int s = 0; s < ksplit; s += N) {
-        float part[N];
+// Part of the gate row of one position into LDS: gw[d] = sum over the ksplit partial rows
+// (stride apart) of the value at base + d, added in split order from 0, for d = d0 + lane + 64 dd
+// (dd < ND). All ND * KS loads of the lane are issued before any sum (indices clamped in range, no
+// branch between the loads): one memory round trip for up to 128 ranks at any split count.
+// KS >= ksplit; the extra loads repeat an in-range address and are not added.
+template <int ND, int KS>
+__device__ __forceinline__ void gate_row(const float *gpart, int ksplit, int64_t stride,
+                                         int64_t base, int r, int rpad, int lane, float *gw,
+                                         int d0 = 0) {
+    float part[ND][KS];
 #pragma unroll
-        for (int q = 0; q < N; ++q) part[q] = gpart[min(s + q, ksplit - 1) * stride + off];
+    for (int dd = 0; dd < ND; ++dd) {
+        const int d = min(d0 + lane + kWave * dd, r - 1);
 #pragma unroll
-        for (int q = 0; q < N; ++q)
-            if (s + q < ksplit) v += part[q];
+        for (int q = 0; q < KS; ++q) part[dd][q] = gpart[min(q, ksplit - 1) * stride + base + d];
     }
-    return v;
+#pragma unroll
+    for (int dd = 0; dd < ND; ++dd) {
+        float v = 0.f;
+#pragma unroll
+        for (int q = 0; q < KS; ++q)
+            if (q < ksplit) v += part[dd][q];
+        const int d = d0 + lane + kWave * dd;
+        if (d < rpad) gw[d] = d < r ? v : 0.f;
+    }
 }
 
 // x = hi + lo, both bf16 rounded to nearest (x - hi is exact in fp32).
@@ -176,16 +189,12 @@ __global__ __launch_bounds__(lat_waves(KT, sizeof(CB)) * kWave) void lattice_ker
                 cid[tj] = j < k ? cand_ids[row * k + j] : 0;
                 u[tj] = j < k ? unary[row * k + j] : 0.f;
             }
-            for (int d = lane; d < rpad; d += kWave) {
-                float v = 0.f;
-                if (d < r) {
-                    const int64_t stride = R * r, off = row * r + d;
-                    v = ksplit == 1   ? sum_parts<1>(gpart, ksplit, stride, off)
-                        : ksplit <= 2 ? sum_parts<2>(gpart, ksplit, stride, off)
-                        : ksplit <= 4 ? sum_parts<4>(gpart, ksplit, stride, off)
-                                      : sum_parts<8>(gpart, ksplit, stride, off);
-                }
-                gw[d] = v;
+            {
+                const int64_t stride = R * r, base = row * r;
+                // 128 ranks per round trip where the codebook chunks are pipelined, else 64
+                constexpr int ND = kPipelined<CB, KT> ? 2 : 1;
+                for (int d0 = 0; d0 < rpad; d0 += ND * kWave)
+                    gate_row<ND, kMaxSplit>(gpart, ksplit, stride, base, r, rpad, lane, gw, d0);
             }
             const bool pok = pid >= 0 && pid < V;
             const uint32_t prow_ok = (uint32_t)__ballot(pok) & 0xFFFFu;  // bit li: row 16ti+li
@@ -199,18 +208,22 @@ __global__ __launch_bounds__(lat_waves(KT, sizeof(CB)) * kWave) void lattice_ker
             // the gate row is in LDS (written by this wave's lanes; LDS is in order per wave)
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
-            // Round trip 2 (per chunk of 64 ranks): the codebook rows; then the MFMA steps.
+            // Round trip 2: the codebook rows, per chunk of 64 ranks. bf16 codebooks and one column
+            // tile: the next chunk's loads are issued before the current chunk's MFMA steps (two
+            // chunks in flight); the other shapes have no registers to spare for that.
             f32x4 acc[KT];
 #pragma unroll
             for (int tj = 0; tj < KT; ++tj) acc[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int c0 = 0; c0 < r; c0 += kRankChunk) {
+            auto chunk_loads = [&](int c0, Seg<CB> &sa, Seg<CB> *sb) {
                 const int seg = c0 + 16 * lg;
                 const int nval = max(0, min(16, r - seg));
                 const bool vseg = vec && nval == 16;
-                Seg<CB> sa, sb[KT];
                 load_seg<CB>(sa, prow, seg, nval, vseg);
 #pragma unroll
                 for (int tj = 0; tj < KT; ++tj) load_seg<CB>(sb[tj], srow[tj], seg, nval, vseg);
+            };
+            auto chunk_mfma = [&](int c0, const Seg<CB> &sa, const Seg<CB> *sb) {
+                const int seg = c0 + 16 * lg;
                 float a[16], gv[16];
                 widen<CB>(sa, a);
 #pragma unroll
@@ -249,6 +262,25 @@ __global__ __launch_bounds__(lat_waves(KT, sizeof(CB)) * kWave) void lattice_ker
                             acc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[t], blo, acc[tj], 0, 0, 0);
                         }
                     }
+                }
+            };
+            if constexpr (kPipelined<CB, KT>) {
+                Seg<CB> sa0, sb0[KT], sa1, sb1[KT];
+                chunk_loads(0, sa0, sb0);
+                for (int c0 = 0; c0 < r; c0 += 2 * kRankChunk) {
+                    const int c1 = c0 + kRankChunk;
+                    if (c1 < r) chunk_loads(c1, sa1, sb1);
+                    chunk_mfma(c0, sa0, sb0);
+                    if (c1 < r) {
+                        if (c1 + kRankChunk < r) chunk_loads(c1 + kRankChunk, sa0, sb0);
+                        chunk_mfma(c1, sa1, sb1);
+                    }
+                }
+            } else {
+                for (int c0 = 0; c0 < r; c0 += kRankChunk) {
+                    Seg<CB> sa, sb[KT];
+                    chunk_loads(c0, sa, sb);
+                    chunk_mfma(c0, sa, sb);
                 }
             }
 
@@ -309,24 +341,42 @@ __global__ __launch_bounds__(lat_waves(KT, sizeof(CB)) * kWave) void lattice_ker
             // after that starts only once this wave has reached the next barrier.
             __syncthreads();
             if (wave == 0) {
+                // best[q][i] for row i = lane, four positions per register (indices < 64 fit a
+                // byte); the chase reads them with v_readlane. The confidences (p_min only) are
+                // read from LDS at the chosen row.
                 const int src = lane < k ? lane : 0;
-                int bj[kLatWaves];
-                float cf[kLatWaves];
+                uint32_t bj[kLatWaves / 4];
 #pragma unroll
-                for (int q = 0; q < kLatWaves; ++q) {
-                    bj[q] = q < np ? best_s[buf][q][src] : 0;
-                    cf[q] = q < np && p_min > 0.f ? conf_s[buf][q][src] : 1.f;
+                for (int g = 0; g < kLatWaves / 4; ++g) {
+                    uint32_t v = 0u;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int q = 4 * g + e;
+                        if (q < np) v |= (uint32_t)best_s[buf][q][src] << (8 * e);
+                    }
+                    bj[g] = v;
                 }
                 int out_j = 0;
+                if (p_min > 0.f) {
 #pragma unroll
-                for (int q = 0; q < kLatWaves; ++q) {
-                    if (q < np) {
-                        const float c = __int_as_float(
-                            __builtin_amdgcn_readlane(__float_as_int(cf[q]), prev));
-                        if (stop == L && c < p_min) stop = p0 + q;
-                        const int j = __builtin_amdgcn_readlane(bj[q], prev);
-                        out_j = lane == q ? j : out_j;
-                        prev = j;
+                    for (int q = 0; q < kLatWaves; ++q) {
+                        if (q < np) {
+                            if (stop == L && conf_s[buf][q][prev] < p_min) stop = p0 + q;
+                            const int j = (int)((__builtin_amdgcn_readlane(bj[q / 4], prev) >>
+                                                 (8 * (q % 4))) & 0xFFu);
+                            out_j = lane == q ? j : out_j;
+                            prev = j;
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < kLatWaves; ++q) {
+                        if (q < np) {
+                            const int j = (int)((__builtin_amdgcn_readlane(bj[q / 4], prev) >>
+                                                 (8 * (q % 4))) & 0xFFu);
+                            out_j = lane == q ? j : out_j;
+                            prev = j;
+                        }
                     }
                 }
                 if (lane < np) {
