@@ -99,6 +99,10 @@ TOPK_CASES = [
     ("signed_zero", 6, 2000, 24, "bf16"),
     ("constant", 3, 4096, 8, "f32"),
     ("ascending", 2, 20000, 16, "f32"),
+    # every element beats the threshold so far: 8 (then 2) units share a workgroup's queue, which
+    # fills up (slots reserved in bulk, waves keeping their own lists, the owner's sorted drains)
+    ("ascending", 2048, 6000, 64, "bf16"),
+    ("ascending", 600, 20000, 32, "f32"),
     ("descending", 2, 20000, 16, "bf16"),
     ("peaked", 64, 151936, 32, "f32"),
     ("high", 5, 70001, 16, "f32"),
