@@ -377,50 +377,134 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_topk_kernel(LmJob job) {
     }
 }
 
-// One workgroup per row: each wave folds a quarter of the row's ranges (keys filtered by its
-// list's k-th key, pairs in range order); wave 0 merges the four lists, combines the pairs in
-// wave order and writes the row.
-__global__ __launch_bounds__(kLmThreads) void lmhead_merge_kernel(
+// One workgroup of kMergeWaves waves per row; the row's ranges are each sorted lists of kLmList
+// keys. Wave w takes ranges [w, w + 1) * ranges / 16 (at most 32, as ranges <= kLmTargetWgs)
+// and loads all their keys at once (lane j holds key j % 16 of ranges r0 + j / 16 + 4 s, s < 8:
+// one memory round trip). A threshold T: the k-th largest of the ranges' first (largest) keys,
+// which are distinct real keys, so the top k of the row are all >= T; and only the ranges whose
+// first key is >= T hold keys >= T. Wave 0 finds T (below) such that at most 64 ranges reach it,
+// so at most kLmList * 64 keys pass; they go to LDS, and wave 0 sorts them (64 at a time,
+// merged) and keeps the top k. The (ref, sum) pairs are combined per wave by a fixed shuffle
+// tree, then over the waves in order.
+constexpr int kMergeWaves = 16;
+constexpr int kMergeSteps = 8;  // 4 ranges per step: 32 ranges per wave
+static_assert(kMergeWaves * (kWave / kLmList) * kMergeSteps >= kLmTargetWgs,
+              "every range of a row has a load slot");
+constexpr int kMergeCands = kLmList * kWave;  // keys >= T at most
+
+// The k-th largest of the 64 lane values (one per lane, 0 = none, nonzero ones distinct): the
+// largest t with at least k lane values >= t, one bit at a time from the top.
+__device__ __forceinline__ uint64_t kth_largest(uint64_t v, int k) {
+    uint64_t t = 0ull;
+    for (int bit = 63; bit >= 0; --bit) {
+        const uint64_t c = t | (1ull << bit);
+        if (__popcll(__ballot(v >= c)) >= k) t = c;
+    }
+    return t;
+}
+
+// A threshold for the n <= 512 distinct first keys in LDS (zeros elsewhere), by one wave: the
+// k-th largest T1 of the 64 lane-wise maxima (k distinct firsts reach it, so every key of the
+// row's top k is >= T1) when at most 64 firsts reach it (the usual case), else the k-th largest
+// of all firsts (exactly k reach it).
+__device__ __forceinline__ uint64_t merge_threshold(const uint64_t *firsts, int k, int lane) {
+    constexpr int J = kLmTargetWgs / kWave;
+    uint64_t f[J], m = 0ull;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        f[j] = firsts[lane + kWave * j];
+        m = kmax(m, f[j]);
+    }
+    const uint64_t t1 = kth_largest(m, k);
+    uint32_t n1 = 0u;
+#pragma unroll
+    for (int j = 0; j < J; ++j) n1 += (uint32_t)__popcll(__ballot(f[j] != 0ull && f[j] >= t1));
+    if (n1 > (uint32_t)kWave) {  // many firsts at or above T1: count all of them per bit
+        uint64_t t = 0ull;
+        for (int bit = 63; bit >= 0; --bit) {
+            const uint64_t c = t | (1ull << bit);
+            int n = 0;
+#pragma unroll
+            for (int j = 0; j < J; ++j) n += __popcll(__ballot(f[j] >= c));
+            if (n >= k) t = c;
+        }
+        return t;
+    }
+    return t1;
+}
+
+__global__ __launch_bounds__(kMergeWaves * kWave) void lmhead_merge_kernel(
     const uint64_t *__restrict__ part_keys, const float2 *__restrict__ part_lse, int ranges, int k,
     int32_t *__restrict__ cand_ids, float *__restrict__ unary, float *__restrict__ lse_out) {
-    __shared__ uint64_t wl[kLmWaves][kWave];
-    __shared__ float2 wp[kLmWaves];
+    __shared__ uint64_t firsts[kLmTargetWgs];   // each range's largest key (0: no range)
+    __shared__ uint64_t cands[kMergeCands];
+    __shared__ uint32_t ncand;
+    __shared__ uint64_t thr;
+    __shared__ float2 wp[kMergeWaves];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t row = blockIdx.x;
-    const int r0 = ranges * wave / kLmWaves, r1 = ranges * (wave + 1) / kLmWaves;
-    uint64_t top = 0ull;  // sorted across the lanes, lane = rank
-    uint64_t tau = 0ull;
-    for (int r = r0; r < r1; r += kWave / kLmList) {  // four ranges of 16 keys per step
-        const int rr = r + lane / kLmList;
-        const uint64_t key = rr < r1 ? part_keys[((size_t)row * ranges + rr) * kLmList + (lane % kLmList)] : 0ull;
-        uint64_t cand = __ballot(key > tau);
-        while (cand != 0ull) {
-            const int src = __builtin_ctzll(cand);
-            cand &= cand - 1ull;
-            const uint64_t c = lane_value(key, src);
-            if (c <= tau) continue;
-            const int p = __popcll(__ballot(top > c));
-            const uint64_t prev = dpp64<kDppWaveShr1>(top);
-            top = lane < p ? top : (lane == p ? c : prev);
-            tau = lane_value(top, k - 1);
+    const int r0 = ranges * wave / kMergeWaves, r1 = ranges * (wave + 1) / kMergeWaves;
+    constexpr int kPer = kWave / kLmList;  // ranges per step
+    uint64_t key[kMergeSteps];
+#pragma unroll
+    for (int st = 0; st < kMergeSteps; ++st) {
+        const int rr = r0 + lane / kLmList + kPer * st;
+        key[st] = rr < r1 ? part_keys[((size_t)row * ranges + rr) * kLmList + (lane % kLmList)]
+                          : 0ull;
+    }
+    const float2 pr = r0 + lane < r1 ? part_lse[(size_t)row * ranges + r0 + lane]
+                                     : make_float2(-INFINITY, 0.f);
+    if (threadIdx.x == 0) ncand = 0u;
+    for (int i = threadIdx.x; i < kLmTargetWgs; i += kMergeWaves * kWave) firsts[i] = 0ull;
+    {  // (ref, sum) of the wave's ranges: lanes 0 .. r1 - r0 - 1, combined by a fixed tree
+        float ref = pr.x, sum = pr.y;
+#pragma unroll
+        for (int d = 1; d < kWave / 2; d *= 2) {
+            const float oref = __shfl_down(ref, d, kWave), osum = __shfl_down(sum, d, kWave);
+            if (lane % (2 * d) == 0) lse_combine(ref, sum, oref, osum);
         }
+        if (lane == 0) wp[wave] = make_float2(ref, sum);
     }
-    float ref = -INFINITY, sum = 0.f;
-    for (int r = r0; r < r1; ++r) {
-        const float2 p = part_lse[(size_t)row * ranges + r];
-        lse_combine(ref, sum, p.x, p.y);
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < kMergeSteps; ++st) {
+        const int rr = r0 + lane / kLmList + kPer * st;
+        if (lane % kLmList == 0 && rr < r1) firsts[rr] = key[st];
     }
-    wl[wave][lane] = top;
-    if (lane == 0) wp[wave] = make_float2(ref, sum);
+    __syncthreads();
+    if (wave == 0) {
+        const uint64_t t = merge_threshold(firsts, k, lane);
+        if (lane == 0) thr = t;
+    }
+    __syncthreads();
+    const uint64_t T = thr;
+    // the keys >= T to LDS
+#pragma unroll
+    for (int st = 0; st < kMergeSteps; ++st) {
+        const bool pass = key[st] != 0ull && key[st] >= T;
+        const uint64_t m = __ballot(pass);
+        if (m == 0ull) continue;
+        uint32_t base = 0u;
+        if (lane == 0)
+            base = __hip_atomic_fetch_add(&ncand, (uint32_t)__popcll(m), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_WORKGROUP);
+        base = __builtin_amdgcn_readfirstlane(base);
+        const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (pass) cands[base + rank] = key[st];
+    }
     __syncthreads();
     if (wave != 0) return;
+    const uint32_t n = __builtin_amdgcn_readfirstlane(ncand);
+    uint64_t top = 0ull;
+    for (uint32_t c0 = 0; c0 < n; c0 += kWave) {
+        const uint64_t c = c0 + lane < n ? cands[c0 + lane] : 0ull;
+        top = wave_merge_desc(top, wave_sort_desc(c, lane), lane);
+    }
+    float ref = -INFINITY, sum = 0.f;
 #pragma unroll
-    for (int w = 1; w < kLmWaves; ++w) top = wave_merge_desc(top, wl[w][lane], lane);
-    ref = -INFINITY;
-    sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kLmWaves; ++w) lse_combine(ref, sum, wp[w].x, wp[w].y);
+    for (int w = 0; w < kMergeWaves; ++w) lse_combine(ref, sum, wp[w].x, wp[w].y);
     const double lse = lse_value(ref, sum);
     if (lane < k) {
         cand_ids[row * k + lane] = key_id(top);
@@ -483,7 +567,7 @@ hipError_t launch_lmhead_topk(const void *hidden, const void *W_lm, int R, int H
         launch_rt<4>(job, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lmhead_merge_kernel, dim3((unsigned)R), dim3(kLmThreads), 0, stream,
+    hipLaunchKernelGGL(lmhead_merge_kernel, dim3((unsigned)R), dim3(kMergeWaves * kWave), 0, stream,
                        job.part_keys, job.part_lse, p.ranges, k, cand_ids, unary, lse);
     return hipGetLastError();
 }
