@@ -942,18 +942,33 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     }
 }
 
-// Merge the S slice results of each row (one wave per row, slices in order).
+// Merge the S slice results of each row (one wave per row, slices in order). The slices' lists
+// and pairs are loaded kMergeAhead at a time before any merge (one memory round trip for S up
+// to that).
+constexpr int kMergeAhead = 8;
+
 __global__ __launch_bounds__(kWave) void topk_merge_kernel(
     int k, int S, const uint64_t *__restrict__ part_keys, const float2 *__restrict__ part_lse,
     int32_t *__restrict__ cand_ids, float *__restrict__ unary, float *__restrict__ lse_out) {
     const int lane = threadIdx.x;
     const int64_t row = blockIdx.x;
-    uint64_t acc = part_keys[row * S * kWave + lane];
-    float2 ls = part_lse[row * S];
-    for (int s = 1; s < S; ++s) {
-        acc = wave_merge_desc(acc, part_keys[(row * S + s) * kWave + lane], lane);
-        const float2 o = part_lse[row * S + s];
-        lse_combine(ls.x, ls.y, o.x, o.y);
+    uint64_t acc = 0ull;
+    float2 ls = make_float2(-INFINITY, 0.f);
+    for (int s0 = 0; s0 < S; s0 += kMergeAhead) {
+        uint64_t keys[kMergeAhead];
+        float2 pr[kMergeAhead];
+#pragma unroll
+        for (int i = 0; i < kMergeAhead; ++i) {
+            const int s = min(s0 + i, S - 1);  // in range; the repeats are not used
+            keys[i] = part_keys[(row * S + s) * kWave + lane];
+            pr[i] = part_lse[row * S + s];
+        }
+#pragma unroll
+        for (int i = 0; i < kMergeAhead; ++i) {
+            if (s0 + i >= S) break;
+            acc = s0 + i == 0 ? keys[i] : wave_merge_desc(acc, keys[i], lane);
+            lse_combine(ls.x, ls.y, pr[i].x, pr[i].y);
+        }
     }
     const double lse = lse_value(ls.x, ls.y);
     if (lane < k) {
