@@ -15,7 +15,8 @@
 //     gate, a reduction kernel) sums the splits in split order: deterministic, no atomics.
 // The top-k kernel can compute the same tiles itself (one per workgroup, before it streams);
 // the results are identical, since the waves' ranges and the summation order are the same.
-// fp32 inputs use a plain fp32 FMA kernel that writes g directly.
+// fp32 inputs use an fp32 FMA kernel (wave-wide dot products per output) that writes g
+// directly.
 #include "device_common.h"
 #include "gate_tile.h"
 #include "kernels.h"
@@ -71,17 +72,26 @@ __global__ __launch_bounds__(256) void gate_reduce_kernel(const float *__restric
 }
 
 // fp32 inputs: one output per thread, fp32 FMA over H in order.
-__global__ __launch_bounds__(256) void gate_f32_kernel(const float *__restrict__ hidden,
-                                                       const float *__restrict__ W, int R, int H,
-                                                       int r, float *__restrict__ g) {
-    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= (int64_t)R * r) return;
-    const int64_t row = e / r;
-    const int c = (int)(e % r);
+// fp32 activations: one workgroup per row; wave w computes columns w, w + 4, ... as wave-wide
+// dot products (lane L adds h[k] W[k][c] for k = L, L + 64, ... in order, then the 64 lane sums
+// are added by a fixed tree), so a row costs one pass over H per column group instead of one
+// thread running over H per output.
+constexpr int kF32Waves = 4;
+
+__global__ __launch_bounds__(kF32Waves * kWave) void gate_f32_kernel(
+    const float *__restrict__ hidden, const float *__restrict__ W, int R, int H, int r,
+    float *__restrict__ g) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t row = blockIdx.x;
     const float *h = hidden + row * H;
-    float acc = 0.f;
-    for (int k = 0; k < H; ++k) acc = fmaf(h[k], W[(int64_t)k * r + c], acc);
-    g[e] = acc;
+    for (int c = wave; c < r; c += kF32Waves) {
+        float acc = 0.f;
+        for (int k = lane; k < H; k += kWave) acc = fmaf(h[k], W[(int64_t)k * r + c], acc);
+#pragma unroll
+        for (int d = kWave / 2; d > 0; d /= 2) acc += __shfl_xor(acc, d, kWave);
+        if (lane == 0) g[row * r + c] = acc;
+    }
 }
 
 template <int NT>
@@ -109,10 +119,9 @@ int gate_splits(int R, int H, int act_dtype) {
 hipError_t launch_gate_partials(const void *hidden, const void *W_sel, int act_dtype, int R,
                                 int H, int r, float *part, hipStream_t stream) {
     if (act_dtype == 0) {
-        const int64_t n = (int64_t)R * r;
-        hipLaunchKernelGGL(gate_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                           stream, static_cast<const float *>(hidden),
-                           static_cast<const float *>(W_sel), R, H, r, part);
+        hipLaunchKernelGGL(gate_f32_kernel, dim3((unsigned)R), dim3(kF32Waves * kWave), 0, stream,
+                           static_cast<const float *>(hidden), static_cast<const float *>(W_sel),
+                           R, H, r, part);
         return hipGetLastError();
     }
     const uint16_t *h = static_cast<const uint16_t *>(hidden);
