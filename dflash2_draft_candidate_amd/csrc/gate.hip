@@ -24,38 +24,37 @@
 namespace dflash2 {
 namespace {
 
-constexpr int kGateThreads = kGateWaves * kWave;
 constexpr int kTargetWgs = 256;
 constexpr int kMaxSplits = 8;  // the consumer adds at most this many partials, all loads at once
 
 template <int NT>
-__global__ __launch_bounds__(kGateThreads) void gate_bf16_kernel(
+__global__ __launch_bounds__(gate_waves<NT>() * kWave) void gate_bf16_kernel(
     const uint16_t *__restrict__ hidden, const uint16_t *__restrict__ W, int R, int H, int r,
     int splits, float *__restrict__ out) {
-    constexpr int NC = NT * 16;
-    __shared__ float red[kGateWaves][16][NC + (NT == 16 ? 0 : 1)];  // <= 64 KB
+    constexpr int GW = gate_waves<NT>();
+    __shared__ float red[GW][16][gate_pitch<NT>()];  // <= 64 KB
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int m = lane & 15, g = lane >> 4;
     int s0, s1;
-    gate_steps(H, blockIdx.y * kGateWaves + wave, splits * kGateWaves, s0, s1);
+    gate_steps(H, blockIdx.y * GW + wave, splits * GW, s0, s1);
     f32x4 acc[NT];
     gate_wave<NT>(hidden, W, R, H, r, blockIdx.x * 16, s0, s1, lane, acc);
 
-    // acc[t][i]: row g*4+i of the tile, column out_col(t, m). Sum the 4 waves in order.
+    // acc[t][i]: row g*4+i of the tile, column out_col(t, m). Sum the GW waves in order.
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) red[wave][g * 4 + i][out_col<NT>(t, m)] = acc[t][i];
     __syncthreads();
     float *dst = out + (int64_t)blockIdx.y * R * r;
-    for (int e = threadIdx.x; e < 16 * r; e += kGateThreads) {
+    for (int e = threadIdx.x; e < 16 * r; e += GW * kWave) {
         const int rr = e / r, c = e % r, orow = blockIdx.x * 16 + rr;
         if (orow >= R) continue;
         float v = red[0][rr][c];
 #pragma unroll
-        for (int w = 1; w < kGateWaves; ++w) v += red[w][rr][c];
+        for (int w = 1; w < GW; ++w) v += red[w][rr][c];
         dst[(int64_t)orow * r + c] = v;
     }
 }
@@ -98,7 +97,7 @@ template <int NT>
 hipError_t launch_bf16(const uint16_t *hidden, const uint16_t *W, int R, int H, int r, int splits,
                        float *out, hipStream_t stream) {
     const dim3 grid((unsigned)((R + 15) / 16), (unsigned)splits);
-    hipLaunchKernelGGL((gate_bf16_kernel<NT>), grid, dim3(kGateThreads), 0, stream, hidden, W, R,
+    hipLaunchKernelGGL((gate_bf16_kernel<NT>), grid, dim3(gate_waves<NT>() * kWave), 0, stream, hidden, W, R,
                        H, r, splits, out);
     return hipGetLastError();
 }
@@ -111,7 +110,7 @@ int gate_splits(int R, int H, int act_dtype) {
     const int64_t nsteps = (H + kStepK - 1) / kStepK;
     int64_t s = (kTargetWgs + mtiles - 1) / mtiles;
     if (s > kMaxSplits) s = kMaxSplits;
-    const int64_t s_max = nsteps / kGateWaves;  // at least one step per wave
+    const int64_t s_max = nsteps / gate_waves<1>();  // at least one step per wave
     if (s > s_max) s = s_max;
     return (int)(s < 1 ? 1 : s);
 }

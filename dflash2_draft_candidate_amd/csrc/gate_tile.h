@@ -22,7 +22,11 @@ namespace dflash2 {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGateWaves = 4;  // waves sharing one tile's range of H
+// Waves sharing one tile's range of H. (Eight waves at 8 column tiles, each with half the
+// steps, took as long: the tile costs the stream the same wave-time either way.)
+template <int NT> constexpr int gate_waves() { return 4; }
+// LDS row pitch (floats) of a wave's part of the tile: padded, except at 16 column tiles (64 KB).
+template <int NT> constexpr int gate_pitch() { return NT * 16 + (NT == 16 ? 0 : 1); }
 constexpr int kStepK = 32;     // H per MFMA
 
 __device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }

@@ -15,8 +15,7 @@ struct TopkPlan {
     int chunk_batches;  // batches per chunk handed to a wave
     int chunks;         // chunks per unit (at most)
 };
-// lds_reserve: dynamic LDS the pass needs besides its chunk sums (the fused gate's tiles).
-TopkPlan plan_topk(int R, int V, int elem_bytes, size_t lds_reserve = 0);
+TopkPlan plan_topk(int R, int V, int elem_bytes);
 size_t topk_workspace_bytes(const TopkPlan &plan, int R);
 // The gate product carried by the top-k pass (bf16 hidden and W_sel, r <= 128): it writes
 // fused_gate_splits(...) partial products [splits][R][r] floats to `part`.

@@ -48,7 +48,9 @@
 //     hidden . W_sel (the same tiles, wave ranges and summation order as the stand-alone gate
 //     kernel) on four of its waves (one per SIMD) before they join the stream; the last of the
 //     four to finish sums their parts through LDS and stores the tile. The work sharing lets the
-//     other twelve waves absorb the delay. Tiles are numbered XCD by XCD (see xcd_major).
+//     other twelve waves absorb the delay. A gate rides along only where its tile parts fit in
+//     LDS beside the chunk sums of the pass's own plan (so select and the stage-by-stage calls
+//     sum the same chunks). Tiles are numbered XCD by XCD (see xcd_major).
 #include "device_common.h"
 #include "gate_tile.h"
 #include "kernels.h"
@@ -64,7 +66,8 @@ constexpr int kThreads = kWaves * kWave;
 constexpr int kMaxUnits = 8;              // units per workgroup (W = kWaves / G >= 2)
 constexpr int kTargetWorkgroups = 256;    // one per CU
 constexpr int kMinBatchesPerWave = 1;     // slices are not cut smaller than this per wave
-constexpr size_t kLdsBudget = 120 * 1024; // dynamic LDS (chunk sums, gate tiles) per workgroup
+constexpr size_t kLdsBudget = 120 * 1024; // chunk sums per workgroup (dynamic LDS)
+constexpr size_t kLdsDynamicMax = 136 * 1024;  // chunk sums + a fused gate's tile parts
 constexpr float kSumLimit = 0x1p100f;     // a chunk sum above this leaves the fast path
 constexpr float kSumFloor = 0x1p-60f;     // so does a unit total below this
 constexpr float kTermMargin = 1.f - 0x1p-10f;  // v_exp_f32 is far more accurate than this
@@ -121,6 +124,9 @@ struct K1Shared {
     uint32_t unit_nch[kMaxUnits];     // and its chunks (0: no unit)
     uint32_t done_all;                // waves that have finished the stream
 };
+static_assert(sizeof(K1Shared) + kLdsDynamicMax <= 160 * 1024, "LDS of a CU (gfx950)");
+
+static_assert(kLdsDynamicMax >= kLdsBudget, "the chunk sums always fit");
 
 // The gate tiles carried by the top-k pass: tile t = sp * mtiles + mt covers rows mt*16 ..
 // mt*16 + 15 over split sp of H, written to part[sp][R][r].
@@ -137,7 +143,9 @@ struct GateJob {
 template <int G> constexpr int gate_first_wave() { return G == 8 ? 8 : 4; }
 
 template <int NT>
-constexpr size_t gate_red_floats() { return NT == 0 ? 0 : (size_t)kGateWaves * 16 * (NT * 16 + 1); }
+constexpr size_t gate_red_floats() {
+    return NT == 0 ? 0 : (size_t)gate_waves<NT>() * 16 * gate_pitch<NT>();
+}
 
 // Workgroups are dispatched to the XCDs round-robin (workgroup g on XCD g % kXcds). Numbering
 // the gate tiles XCD by XCD gives each XCD a run of consecutive tiles (m-tiles of one or two
@@ -152,12 +160,13 @@ __device__ __forceinline__ int xcd_major(int g, int n) {
 template <int NT>
 __device__ __forceinline__ void gate_tile_part(const GateJob &gj, int gw, int lane, float *red,
                                             uint32_t *arrived) {
-    constexpr int PITCH = NT * 16 + 1;
+    constexpr int PITCH = gate_pitch<NT>();
     const int t = xcd_major(blockIdx.x, gridDim.x);
     if (t >= gj.mtiles * gj.splits) return;
     const int mt = t % gj.mtiles, sp = t / gj.mtiles;
     int s0, s1;
-    gate_steps(gj.H, sp * kGateWaves + gw, gj.splits * kGateWaves, s0, s1);
+    constexpr int GW = gate_waves<NT>();
+    gate_steps(gj.H, sp * GW + gw, gj.splits * GW, s0, s1);
     f32x4 acc[NT];
     gate_wave<NT>(gj.hidden, gj.W, gj.R, gj.H, gj.r, mt * 16, s0, s1, lane, acc);
     const int m = lane & 15, g = lane >> 4;
@@ -168,7 +177,7 @@ __device__ __forceinline__ void gate_tile_part(const GateJob &gj, int gw, int la
     uint32_t a = 0u;
     if (lane == 0)
         a = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (__builtin_amdgcn_readfirstlane(a) != kGateWaves - 1) return;
+    if (__builtin_amdgcn_readfirstlane(a) != GW - 1) return;
     // the last of the four: every part is in LDS; add them in wave order
     float *dst = gj.part + (int64_t)sp * gj.R * gj.r;
     for (int e = lane; e < 16 * gj.r; e += kWave) {
@@ -176,7 +185,7 @@ __device__ __forceinline__ void gate_tile_part(const GateJob &gj, int gw, int la
         if (orow >= gj.R) continue;
         float v = red[rr * PITCH + c];
 #pragma unroll
-        for (int w = 1; w < kGateWaves; ++w) v += red[(w * 16 + rr) * PITCH + c];
+        for (int w = 1; w < GW; ++w) v += red[(w * 16 + rr) * PITCH + c];
         dst[(int64_t)orow * gj.r + c] = v;
     }
 }
@@ -574,7 +583,7 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     __syncthreads();  // the only barrier before the stream (every wave arrives long before data)
 
     if constexpr (NTG > 0) {
-        if (wave >= gate_first_wave<G>() && wave < gate_first_wave<G>() + kGateWaves)
+        if (wave >= gate_first_wave<G>() && wave < gate_first_wave<G>() + gate_waves<NTG>())
             gate_tile_part<NTG>(gj, wave - gate_first_wave<G>(), lane,
                                 chunk_sums + (size_t)G * nch_max * kWave, &sh.gate_arrived);
     }
@@ -721,7 +730,7 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     // with at most one batch per wave (the threshold would come after every batch is read).
     const bool has_tile = NTG > 0 && xcd_major(blockIdx.x, gridDim.x) < gj.mtiles * gj.splits;
     auto gate_slot = [&](int s) {
-        return has_tile && s >= gate_first_wave<G>() && s < gate_first_wave<G>() + kGateWaves;
+        return has_tile && s >= gate_first_wave<G>() && s < gate_first_wave<G>() + gate_waves<NTG>();
     };
     if (active) {
         const uint32_t mk = sh.seed_vals[wave * kWave + lane];
@@ -1031,7 +1040,7 @@ hipError_t launch_k1(const TopkPlan &plan, const void *logits, int R, int V, int
 
 }  // namespace
 
-TopkPlan plan_topk(int R, int V, int elem_bytes, size_t lds_reserve) {
+TopkPlan plan_topk(int R, int V, int elem_bytes) {
     const int64_t EV = 16 / elem_bytes;
     const int64_t nvec_row = V / EV + 1;  // whole vectors of a row, rounded up
     const int64_t nb_row = (nvec_row + kStep - 1) / kStep;
@@ -1057,7 +1066,7 @@ TopkPlan plan_topk(int R, int V, int elem_bytes, size_t lds_reserve) {
     for (;;) {
         p.chunks = (int)((nb_unit + p.chunk_batches - 1) / p.chunk_batches);
         if (p.chunks < 1) p.chunks = 1;
-        if (chunk_sum_bytes(p.groups, p.chunks) + lds_reserve <= kLdsBudget) break;
+        if (chunk_sum_bytes(p.groups, p.chunks) <= kLdsBudget) break;
         p.chunk_batches *= 2;
     }
     return p;
@@ -1071,7 +1080,11 @@ size_t topk_workspace_bytes(const TopkPlan &p, int R) {
 int fused_gate_splits(int R, int V, int logits_dtype, int H, int r) {
     const int nt = fused_gate_nt(r);
     if (nt == 0) return 0;
-    const TopkPlan plan = plan_topk(R, V, logits_dtype == 0 ? 4 : 2, gate_red_bytes(nt));
+    // The plan (its chunks above all) is the one the pass has without a gate, so both give the
+    // same logsumexp bit for bit; the gate rides along only where its tile parts fit beside the
+    // chunk sums.
+    const TopkPlan plan = plan_topk(R, V, logits_dtype == 0 ? 4 : 2);
+    if (chunk_sum_bytes(plan.groups, plan.chunks) + gate_red_bytes(nt) > kLdsDynamicMax) return 0;
     // one tile per workgroup; the grid holds at least R / 8 >= mtiles workgroups
     const int mtiles = (R + 15) / 16;
     const int most = k1_grid(plan, R) / mtiles;
@@ -1084,7 +1097,7 @@ hipError_t launch_topk_lse(const void *logits, int logits_dtype, int R, int V, i
                            hipStream_t stream, const FusedGate *gate) {
     const int nt = gate ? fused_gate_nt(gate->r) : 0;
     if (gate && nt == 0) return hipErrorInvalidValue;
-    const TopkPlan plan = plan_topk(R, V, logits_dtype == 0 ? 4 : 2, gate_red_bytes(nt));
+    const TopkPlan plan = plan_topk(R, V, logits_dtype == 0 ? 4 : 2);
     uint64_t *part_keys = static_cast<uint64_t *>(workspace);
     float2 *part_lse = reinterpret_cast<float2 *>(part_keys + (size_t)R * plan.slices * kWave);
     GateJob gj{};

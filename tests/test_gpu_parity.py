@@ -389,7 +389,10 @@ def test_select_shapes(lib, ref, B, L, V, H, r, k, ld, ad, cd, recipe):
 
 STAGED = [("qwen3-8b-b1", None), ("serving-b64", None), ("gemma4-31b", None),
           ("case", (3, 5, 1021, 100, 24, 7, "bf16", "bf16", "bf16", "normal")),
-          ("case", (2, 9, 3000, 520, 40, 5, "f32", "bf16", "f32", "normal"))]
+          ("case", (2, 9, 3000, 520, 40, 5, "f32", "bf16", "f32", "normal")),
+          # chunk sums of 113 KB beside the gate's tile parts: the fused pass keeps the chunks
+          # of the pass without a gate
+          ("case", (64, 16, 230000, 512, 64, 16, "bf16", "bf16", "bf16", "normal"))]
 
 
 @pytest.mark.parametrize("name,shape", STAGED, ids=[n if c is None else "-".join(map(str, c))
