@@ -20,8 +20,9 @@
 //   * Product. v_mfma_f32_16x16x32_bf16 with fp32 accumulation. Both operands are K-contiguous
 //     (rows of hidden for A, rows of W_lm for B): per step of 64 h a lane loads 16 consecutive
 //     h of each of its rows (32 bytes; a row's four lane groups read a whole 128-byte line) and
-//     feeds them to two MFMAs; two steps of loads are in flight. H % 8 == 0; rows past R read
-//     row R - 1 and are dropped; tiles past a wave's run issue no loads.
+//     feeds them to two MFMAs; four steps of loads are in flight (fewer for larger row tiles).
+//     H % 8 == 0; rows past R read row R - 1 and are dropped; tiles past a wave's run issue no
+//     loads.
 //   * Epilogue. The accumulator of tile (rt, ct) puts row 16 rt + 4 g + t (g = lane / 16) and
 //     column 16 ct + (lane % 16) in each lane, so every row lives in one lane group of 16. Each
 //     lane keeps an online logsumexp pair (reference = its largest value, log2 domain) per row;
@@ -220,7 +221,7 @@ struct LmJob {
 // Workgroup (row block, range): the row block of one range on one XCD (see the header).
 template <int RT>
 __global__ __launch_bounds__(kLmThreads) void lmhead_topk_kernel(LmJob job) {
-    constexpr int D = RT == 4 ? 1 : 2;  // steps of loads in flight
+    constexpr int D = RT == 4 ? 1 : (RT == 1 ? 4 : 2);  // steps of loads in flight (registers)
     __shared__ uint64_t lists[kLmWaves][16 * RT][16];
     __shared__ float2 pairs[kLmWaves][16 * RT];
 
