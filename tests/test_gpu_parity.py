@@ -131,7 +131,8 @@ def test_topk_lse(lib, ref, case, R, V, k, dtype):
 
 GATE_CASES = [(4, 64, 16, "f32"), (16, 4096, 64, "bf16"), (1024, 4096, 64, "bf16"),
               (33, 100, 24, "bf16"), (5, 5376, 128, "bf16"), (17, 256, 256, "bf16"),
-              (3, 40, 1, "bf16"), (2048, 4096, 64, "bf16"), (7, 300, 33, "f32")]
+              (3, 40, 1, "bf16"), (2048, 4096, 64, "bf16"), (7, 300, 33, "f32"),
+              (65, 2000, 130, "f32")]  # fp32: several columns per wave, H well past 64
 
 
 @pytest.mark.parametrize("R,H,r,dtype", GATE_CASES, ids=[f"R{a}-H{b}-r{c}-{d}" for a, b, c, d in GATE_CASES])
