@@ -373,6 +373,9 @@ SMALL_SELECT = [
     (2, 7, 4099, 64, 40, 64, "f32", "bf16", "f32", "normal"),
     (1, 70, 2000, 64, 64, 16, "bf16", "bf16", "bf16", "normal"),
     (2, 9, 3001, 48, 20, 50, "bf16", "f32", "bf16", "normal"),
+    # r = 100: two ragged rank chunks and two gate trips per row in the lattice (fp32 codebooks),
+    # and the fused gate's ragged-column path (8 column tiles over 100 columns)
+    (2, 5, 3000, 96, 100, 16, "f32", "bf16", "f32", "normal"),
 ]
 
 
