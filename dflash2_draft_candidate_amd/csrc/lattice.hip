@@ -12,10 +12,13 @@
 //
 // Per position the lattice is a small product E = (P * g) S^T with P, S the gathered [k, r]
 // codebook rows: it runs on the matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation). The
-// fp32 operand a = P * g is split into two bf16 values, a = hi + lo + O(2^-18 |a|) (both rounded
-// to nearest), and each is multiplied exactly (bf16 x bf16 fits fp32) by the bf16 codebook
-// value; fp32 codebooks are split the same way (hi*hi + lo*hi + hi*lo, the lo*lo term is below
-// 2^-16 |a b|). A wave owns one position and one 16-row tile of predecessors
+// fp32 operand a = P * g is split into three bf16 values, a = a1 + a2 + a3 + O(2^-27 |a|) (each
+// rounded to nearest from the exact remainder), and each part is multiplied exactly (bf16 x bf16
+// fits fp32) by the bf16 codebook value: three MFMAs per step, with the operand as accurate as an
+// fp32 product. fp32 codebooks are split the same way and the six part products down to 2^-18
+// |a b| are kept (a1b1, a2b1, a1b2, a3b1, a2b2, a1b3; the rest are below 2^-27 |a b|). With only
+// two parts the remainder (2^-18 |a|) is large enough to break the 1e-5 edge tolerance where few
+// ranks carry large codebook values. A wave owns one position and one 16-row tile of predecessors
 // (KT = ceil(k / 16) waves per position) and all KT column tiles. The rank is cut into chunks of
 // 64: within a chunk, lane group g = lane / 16 holds ranks 16g .. 16g + 15 of its rows, and MFMA
 // step t (of 2) takes ranks 16g + 8t .. 16g + 8t + 7 as its K slots 8g .. 8g + 7 (any assignment
@@ -80,10 +83,12 @@ __device__ __forceinline__ void load_seg(Seg<CB> &s, const CB *row, int seg, int
     for (int q = 0; q < Seg<CB>::NV; ++q) s.v[q] = *reinterpret_cast<const u32x4 *>(tmp + q * Seg<CB>::EV);
 }
 
+// Ranks 8t .. 8t + 7 of a segment, widened to fp32.
 template <typename CB>
-__device__ __forceinline__ void widen(const Seg<CB> &s, float *x) {
+__device__ __forceinline__ void widen_half(const Seg<CB> &s, int t, float *x) {
 #pragma unroll
-    for (int q = 0; q < Seg<CB>::NV; ++q) Elem<CB>::unpack(s.v[q], x + q * Seg<CB>::EV);
+    for (int q = 0; q < Seg<CB>::NV / 2; ++q)
+        Elem<CB>::unpack(s.v[t * (Seg<CB>::NV / 2) + q], x + q * Seg<CB>::EV);
 }
 
 // Part of the gate row of one position into LDS: gw[d] = sum over the ksplit partial rows
@@ -113,13 +118,18 @@ __device__ __forceinline__ void gate_row(const float *gpart, int ksplit, int64_t
     }
 }
 
-// x = hi + lo, both bf16 rounded to nearest (x - hi is exact in fp32).
-__device__ __forceinline__ void split_bf16(const float *x, bf16x8 *hi, bf16x8 *lo) {
+// x = x1 + x2 + x3 + O(2^-27 |x|), each bf16 rounded to nearest (every remainder is exact in
+// fp32), for N values (N / 8 fragments each).
+template <int N>
+__device__ __forceinline__ void split3_bf16(const float *x, bf16x8 *x1, bf16x8 *x2, bf16x8 *x3) {
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-        const __bf16 h = (__bf16)x[s];
-        hi[s / 8][s % 8] = h;
-        lo[s / 8][s % 8] = (__bf16)(x[s] - (float)h);
+    for (int s = 0; s < N; ++s) {
+        const __bf16 h1 = (__bf16)x[s];
+        const float r1 = x[s] - (float)h1;
+        const __bf16 h2 = (__bf16)r1;
+        x1[s / 8][s % 8] = h1;
+        x2[s / 8][s % 8] = h2;
+        x3[s / 8][s % 8] = (__bf16)(r1 - (float)h2);
     }
 }
 
@@ -224,42 +234,38 @@ __global__ __launch_bounds__(lat_waves(KT, sizeof(CB)) * kWave) void lattice_ker
             };
             auto chunk_mfma = [&](int c0, const Seg<CB> &sa, const Seg<CB> *sb) {
                 const int seg = c0 + 16 * lg;
-                float a[16], gv[16];
-                widen<CB>(sa, a);
+                // one half of the 16 ranks at a time: its three bf16 parts, then every tile's MFMAs
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 t = *reinterpret_cast<const float4 *>(gw + seg + 4 * q);
-                    gv[4 * q] = t.x; gv[4 * q + 1] = t.y; gv[4 * q + 2] = t.z; gv[4 * q + 3] = t.w;
-                }
+                for (int t = 0; t < 2; ++t) {
+                    float a[8];
+                    widen_half<CB>(sa, t, a);
 #pragma unroll
-                for (int s = 0; s < 16; ++s) a[s] *= gv[s];
-                bf16x8 ahi[2], alo[2];
-                split_bf16(a, ahi, alo);
+                    for (int q = 0; q < 2; ++q) {
+                        const float4 gq = *reinterpret_cast<const float4 *>(gw + seg + 8 * t + 4 * q);
+                        a[4 * q] *= gq.x; a[4 * q + 1] *= gq.y; a[4 * q + 2] *= gq.z; a[4 * q + 3] *= gq.w;
+                    }
+                    bf16x8 a1[1], a2[1], a3[1];
+                    split3_bf16<8>(a, a1, a2, a3);
 #pragma unroll
-                for (int tj = 0; tj < KT; ++tj) {
-                    if constexpr (sizeof(CB) == 2) {  // bf16 codebook: exact operands
-#pragma unroll
-                        for (int t = 0; t < 2; ++t) {
+                    for (int tj = 0; tj < KT; ++tj) {
+                        if constexpr (sizeof(CB) == 2) {  // bf16 codebook: exact operand
                             const bf16x8 bv = __builtin_bit_cast(bf16x8, sb[tj].v[t]);
-                            acc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[t], bv, acc[tj], 0, 0, 0);
-                            acc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[t], bv, acc[tj], 0, 0, 0);
-                        }
-                    } else {
-#pragma unroll
-                        for (int t = 0; t < 2; ++t) {
+                            acc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[0], bv, acc[tj], 0, 0, 0);
+                            acc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2[0], bv, acc[tj], 0, 0, 0);
+                            acc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a3[0], bv, acc[tj], 0, 0, 0);
+                        } else {
+                            // both operands split in three; the products kept are those down to
+                            // 2^-18 of a b (the others are below 2^-27 |a b|)
                             float bv[8];
-                            Elem<CB>::unpack(sb[tj].v[2 * t], bv);
-                            Elem<CB>::unpack(sb[tj].v[2 * t + 1], bv + 4);
-                            bf16x8 bhi, blo;
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const __bf16 h = (__bf16)bv[e];
-                                bhi[e] = h;
-                                blo[e] = (__bf16)(bv[e] - (float)h);
-                            }
-                            acc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[t], bhi, acc[tj], 0, 0, 0);
-                            acc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[t], bhi, acc[tj], 0, 0, 0);
-                            acc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[t], blo, acc[tj], 0, 0, 0);
+                            widen_half<CB>(sb[tj], t, bv);
+                            bf16x8 b1[1], b2[1], b3[1];
+                            split3_bf16<8>(bv, b1, b2, b3);
+                            acc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[0], b1[0], acc[tj], 0, 0, 0);
+                            acc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2[0], b1[0], acc[tj], 0, 0, 0);
+                            acc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[0], b2[0], acc[tj], 0, 0, 0);
+                            acc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a3[0], b1[0], acc[tj], 0, 0, 0);
+                            acc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2[0], b2[0], acc[tj], 0, 0, 0);
+                            acc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[0], b3[0], acc[tj], 0, 0, 0);
                         }
                     }
                 }
