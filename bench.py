@@ -13,7 +13,8 @@ Prints one JSON line:
                (R*V*elem + R*k*8 + R*4) / mean K1 launch time (HIP events around a loop of K1-only
                launches on the launch stream), against the MI355X HBM peak of 8 TB/s; `traffic`
                comes from committed rocprofv3 counter readings when they match the current kernel
-  cpu_baseline the fp64 C oracle (single-threaded) on the host, on the same workload
+  cpu_baseline the fp64 C oracle on the host, on the same workload: row-parallel over the host's
+               cores (value, cores) and single-threaded (single_thread), with the CPU model
   per_config   end-to-end latency and K1 bandwidth of every workload
   extras       the default workload with the walk's sampling and p_min modes, the grouped
                dynamic depthwise convolution at the serving block shape, and the LM-head product
@@ -109,9 +110,12 @@ class Workload:
             raise RuntimeError(f"dflash2_topk_lse failed with status {rc}")
 
 
-def time_loop(fn, steps: int, warmup: int, warm_seconds: float = WARM_SECONDS) -> float:
+def time_loop(fn, steps: int, warmup: int, warm_seconds: float = WARM_SECONDS,
+              stats: dict | None = None) -> float:
     """Mean milliseconds per call of fn(i), HIP events on the current stream, after `warmup`
-    untimed calls and as many more as fill warm_seconds."""
+    untimed calls and as many more as fill warm_seconds. With `stats`, an event is also recorded
+    between consecutive calls and the per-call median, p10 and p90 go into it (the event records
+    are enqueued between launches, so the mean of the per-call times is the same region)."""
     import torch
     t0 = time.time()
     i = 0
@@ -121,21 +125,30 @@ def time_loop(fn, steps: int, warmup: int, warm_seconds: float = WARM_SECONDS) -
         if i % 64 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
+    n_ev = steps + 1 if stats is not None else 2
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ev[0].record()
     for j in range(steps):
         fn(i + j)
-    e1.record()
+        if stats is not None:
+            ev[j + 1].record()
+    ev[-1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    total = ev[0].elapsed_time(ev[-1])
+    if stats is not None:
+        per = sorted(ev[j].elapsed_time(ev[j + 1]) for j in range(steps))
+        q = lambda f: per[min(steps - 1, int(round(f * (steps - 1))))]
+        stats.update({"median_us": round(q(0.5) * 1e3, 2), "p10_us": round(q(0.1) * 1e3, 2),
+                      "p90_us": round(q(0.9) * 1e3, 2)})
+    return total / steps
 
 
 def measure(name: str, device: str, steps: int, warmup: int) -> dict:
     import torch
     w = Workload(name, device)
     s = w.s
-    e2e_ms = time_loop(w.step, steps, warmup)
+    e2e_stats, k1_stats = {}, {}
+    e2e_ms = time_loop(w.step, steps, warmup, stats=e2e_stats)
     ids = torch.empty((s.R, s.k), dtype=torch.int32, device=device)
     unary = torch.empty((s.R, s.k), dtype=torch.float32, device=device)
     lse = torch.empty((s.R,), dtype=torch.float32, device=device)
@@ -144,12 +157,14 @@ def measure(name: str, device: str, steps: int, warmup: int) -> dict:
     wsb = d2.library().dflash2_topk_lse_workspace_bytes(s.R, s.V, s.k,
                                                         BF16 if s.logits_dtype == "bf16" else F32)
     ws = torch.empty(max(16, wsb), dtype=torch.uint8, device=device)
-    k1_ms = time_loop(lambda i: w.k1_step(i, ids, unary, lse, ws), steps, warmup)
+    k1_ms = time_loop(lambda i: w.k1_step(i, ids, unary, lse, ws), steps, warmup,
+                      stats=k1_stats)
     gbs = k1_bytes(s) / (k1_ms * 1e-3) / 1e9
     res = {"B": s.B, "L": s.L, "k": s.k, "V": s.V, "H": s.H, "r": s.r,
            "logits": s.logits_dtype, "e2e_us": round(e2e_ms * 1e3, 2),
            "positions_per_s": round(s.R / (e2e_ms * 1e-3), 1), "k1_us": round(k1_ms * 1e3, 2),
-           "k1_gbs": round(gbs, 1), "k1_frac": round(gbs / PEAK_HBM_GBS, 4)}
+           "k1_gbs": round(gbs, 1), "k1_frac": round(gbs / PEAK_HBM_GBS, 4),
+           "e2e_us_per_step": e2e_stats, "k1_us_per_step": k1_stats}
     res["_workload"] = w
     return res
 
@@ -233,23 +248,72 @@ def measure_lmhead(device: str, steps: int, warmup: int) -> dict:
             "unfused_matmul_plus_topk_us": round(ms_unfused * 1e3, 2)}
 
 
-def cpu_baseline(name: str, min_seconds: float = 12.0, max_passes: int = 64) -> dict:
-    """The oracle (fp64 C, one thread) on the host over whole passes of the workload."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads(cap: int) -> int:
+    """Threads for the row-parallel oracle: the cores this process may run on, no more than
+    OMP_NUM_THREADS when that is set (the host's share of cores per GPU), nor than `cap`."""
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, min(n, cap))
+
+
+def cpu_baseline(name: str, seconds_1: float = 8.0, seconds_n: float = 6.0,
+                 max_passes: int = 512) -> dict:
+    """The oracle (fp64 C) on the host over whole passes of the workload: single-threaded, then
+    row-parallel (the sequences split into contiguous groups, one oracle call per group on a pool
+    of threads; ctypes releases the GIL during each call, and sequences are independent, so the
+    outputs are those of the single-threaded pass, which is checked)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
     import oracle
     import synth
     x = synth.make_inputs(name)
     o = oracle.default()
-    passes, elapsed = 0, 0.0
-    while passes < max_passes and (passes == 0 or elapsed < min_seconds):
+    B, R = x.spec.B, x.spec.R
+
+    def run(b0, b1):
+        return o.select(x.logits[b0:b1], x.hidden[b0:b1], x.W_sel, x.pred_cb, x.succ_cb,
+                        x.anchor_ids[b0:b1], x.spec.k)
+
+    passes1, el1, ref = 0, 0.0, None
+    while passes1 < max_passes and (passes1 == 0 or el1 < seconds_1):
         t0 = time.perf_counter()
-        o.select(x.logits, x.hidden, x.W_sel, x.pred_cb, x.succ_cb, x.anchor_ids, x.spec.k)
-        elapsed += time.perf_counter() - t0
-        passes += 1
-    R = x.spec.R
-    return {"value": round(R * passes / elapsed, 1), "unit": "positions/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{passes} full pass(es) of the {name} workload ({R} positions each), "
-                      f"{elapsed:.1f} s total, single-threaded fp64 C"}
+        ref = run(0, B)
+        el1 += time.perf_counter() - t0
+        passes1 += 1
+    n = host_threads(B)
+    bounds = [(B * i // n, B * (i + 1) // n) for i in range(n)]
+    passesn, eln, parts = 0, 0.0, None
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        while passesn < max_passes and (passesn == 0 or eln < seconds_n):
+            t0 = time.perf_counter()
+            parts = list(ex.map(lambda bb: run(*bb), bounds))
+            eln += time.perf_counter() - t0
+            passesn += 1
+    got = np.concatenate([p.path for p in parts])
+    if not np.array_equal(got, ref.path) or \
+            not np.array_equal(np.concatenate([p.cand_ids for p in parts]), ref.cand_ids):
+        raise RuntimeError("row-parallel oracle differs from the single-threaded pass")
+    v1, vn = R * passes1 / el1, R * passesn / eln
+    return {"value": round(vn, 1), "unit": "positions/s", "cores": n, "kind": "oracle",
+            "sample": f"{passesn} full pass(es) of the {name} workload ({R} positions each) in "
+                      f"{eln:.1f} s, {n} threads, row-parallel fp64 C (sequences split over the "
+                      f"threads)",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "single_thread": {"value": round(v1, 1), "unit": "positions/s", "cores": 1,
+                              "sample": f"{passes1} full pass(es) in {el1:.1f} s"}}
 
 
 def committed_traffic() -> dict | None:

@@ -206,9 +206,11 @@ struct WaveTopk {
     bool spilled;          // a non-owner that had to keep candidates itself
 };
 
+// Key 0 (no threshold yet) admits every element: its logit is -inf, not the NaN the key map
+// would give (a NaN threshold would fail every comparison and drop candidates).
 __device__ __forceinline__ void set_tau(WaveTopk &w, uint64_t key) {
     w.tau_key = key;
-    w.tau_v = key_logit(key);
+    w.tau_v = key == 0ull ? -INFINITY : key_logit(key);
 }
 
 // A valid threshold `key` was found: adopt it and publish it to the unit.
@@ -849,6 +851,13 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
                 w.home = pq == q;
                 set_tau(w, 0ull);
                 te_key = ~0ull;
+                // A helper offers nothing before the unit's seed is in its threshold (without
+                // it every element would be a candidate). The unit's seeding waves reach the
+                // seed without waiting on any other wave, so this wait ends.
+                while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                           &sh.seed_done[pq], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) ==
+                       0u)
+                    __builtin_amdgcn_s_sleep(1);
             }
             if (w.owner) drain<false>(w, lane, false);
             pull_tau(w);

@@ -22,12 +22,16 @@ its logits, hidden rows and anchor; W_sel and the codebooks use the base seed):
 * qwen3-8b-b1 / serving-b64: logits ~ N(0, 3^2), 8 distinct tokens per row get +U[4, 8].
 * gemma4-31b: logits ~ N(0, 2^2), 32 distinct tokens per row get the Zipf(s=1.1)-ranked boost
   8 * i^-1.1 for i = 1..32.
-* stress: logits ~ N(0, 0.1^2) in every row. Even rows (global row index b*L+p) are near-flat with
-  a planted ladder: k-4 tokens at 1 + 0.125*(k-4-j) (j = 0..k-5) whose top two share one value,
-  then a cluster of 8 tokens at exactly 1.0, which straddles the k-th place, so the top-k keeps
-  the 4 cluster tokens with the lowest ids. Odd rows are sharply peaked: one token gets +12 and
-  its value is copied onto a second token (an exact tie at the top); 16 further token pairs get
-  copied values (exact ties in the body).
+* stress: logits ~ N(0, 0.1^2) in every row. Even rows (global row index b*L+p) stay near-flat;
+  odd rows are sharply peaked: one uniform token gets +12. Exact ties are then planted in every
+  row by copying values onto tokens outside the row's top k+2: in near-flat rows the value at
+  rank 0 (a tie at the top), then in every row the value at rank floor(k/2) (a tie inside the
+  top k), then the value at rank k-1 (ranks taken after the earlier copies), so that pair
+  straddles the k-th place and the lower id of the two is kept.
+* ladder (a parity recipe, not a workload): as stress's base, but even rows carry a planted
+  ladder of k-4 tokens at 1 + 0.125*(k-4-j) (j = 0..k-5) whose top two share one value, then a
+  cluster of 8 tokens at exactly 1.0 straddling the k-th place; odd rows get one token at +12
+  copied onto a second token and 16 further copied pairs.
 * Sums are formed in fp32 and rounded once to bf16 (round to nearest even) where the stored dtype
   is bf16. bf16 tensors are numpy ``uint16`` arrays of raw bits.
 
@@ -146,7 +150,7 @@ class Spec:
     logits_dtype: str  # "f32" | "bf16"
     act_dtype: str     # hidden and W_sel
     cb_dtype: str      # pred_cb and succ_cb
-    recipe: str        # "tiny" | "boost8" | "zipf32" | "stress" | "normal"
+    recipe: str        # "tiny" | "boost8" | "zipf32" | "stress" | "ladder" | "normal"
     seed: int
 
     @property
@@ -214,6 +218,15 @@ def _logit_rows(s: Spec, b: int) -> np.ndarray:
             x[p, ids[p]] += boost
     elif s.recipe == "stress":
         x = normal(sb, S_LOGITS, L * V, std=0.1).reshape(L, V)
+        peak = index(sb, S_BOOST_IDS, L, V)
+        draws = index(sb, S_TIES, L * 64, V).reshape(L, 64)
+        for p in range(L):
+            flat = (b * L + p) % 2 == 0
+            if not flat:
+                x[p, peak[p]] += np.float32(12.0)
+            _plant_ties(x[p], k, flat, draws[p])
+    elif s.recipe == "ladder":
+        x = normal(sb, S_LOGITS, L * V, std=0.1).reshape(L, V)
         m = k + 4
         ids = distinct_ids(sb, S_TIES, L, V, max(m, 34))
         for p in range(L):
@@ -234,6 +247,43 @@ def _logit_rows(s: Spec, b: int) -> np.ndarray:
     else:
         raise ValueError(f"unknown recipe {s.recipe}")
     return x
+
+
+def _plant_ties(row: np.ndarray, k: int, flat: bool, draws: np.ndarray) -> None:
+    """Copy values of the row's leading tokens onto tokens outside its top k+2 (in place): rank 0
+    (near-flat rows only), then rank floor(k/2), then rank k-1, each rank taken after the earlier
+    copies. Ranks follow the stored values (larger first, lower id first among equal ones); the
+    targets come from `draws` (seeded ids), skipping tokens already among the leaders."""
+    V = row.size
+    m = min(k + 2, V)
+    if m < 2:
+        return
+    lead = np.argpartition(-row, m - 1)[:m]
+    top = sorted(((float(row[i]), int(i)) for i in lead), key=lambda t: (-t[0], t[1]))
+    used = {i for _, i in top}
+    it = iter(draws.tolist())
+
+    def target() -> int | None:
+        for t in it:
+            if t not in used:
+                used.add(t)
+                return t
+        for t in range(V):  # (only for tiny rows: the seeded draws ran out)
+            if t not in used:
+                used.add(t)
+                return t
+        return None
+
+    for rank in ([0] if flat else []) + [k // 2, k - 1]:
+        if rank >= len(top):
+            continue
+        t = target()
+        if t is None:
+            return
+        v = top[rank][0]
+        row[t] = np.float32(v)
+        top.append((v, t))
+        top.sort(key=lambda e: (-e[0], e[1]))
 
 
 def make_inputs(s: Spec | str, **overrides) -> Inputs:

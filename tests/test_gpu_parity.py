@@ -110,6 +110,10 @@ TOPK_CASES = [
     ("low", 5, 70001, 16, "bf16"),
     ("mixed_range", 24, 40000, 16, "f32"),
     ("mixed_range", 1030, 3000, 8, "bf16"),
+    # rows not a multiple of the units per workgroup at the full vocabulary: the last workgroup's
+    # idle waves help other units from their first batch on, before those units have a threshold
+    ("normal", 1030, 151936, 16, "bf16"),
+    ("peaked", 515, 151936, 16, "f32"),
     ("wide", 3, 50000, 64, "f32"),
 ]
 
@@ -379,8 +383,12 @@ SMALL_SELECT = [
     # one or five ranks carrying large codebook values: a two-part bf16 split of the lattice
     # operand errs by up to 3x the edge tolerance here (a numpy model of that arithmetic on these
     # inputs), the three-part split by under 0.06x
-    (6, 33, 1000, 200, 1, 64, "f32", "f32", "bf16", "stress"),
-    (6, 33, 1000, 200, 5, 64, "f32", "f32", "f32", "stress"),
+    (6, 33, 1000, 200, 1, 64, "f32", "f32", "bf16", "ladder"),
+    (6, 33, 1000, 200, 5, 64, "f32", "f32", "f32", "ladder"),
+    # odd L and B*L >= 512 rows not a multiple of the units per workgroup (idle helper waves)
+    (103, 5, 151936, 64, 16, 16, "bf16", "bf16", "bf16", "boost8"),
+    # the planted-ladder recipe: every even row's top k separated far above a flat bulk
+    (16, 8, 151936, 64, 64, 32, "f32", "bf16", "bf16", "ladder"),
 ]
 
 

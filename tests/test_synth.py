@@ -84,8 +84,63 @@ def test_workload_shapes_and_dtypes():
     assert (x.anchor_ids >= 0).all() and (x.anchor_ids < 151936).all()
 
 
-def test_stress_planted_ties():
+def _order(row: np.ndarray) -> np.ndarray:
+    """Ids of the row in the candidate order: larger value first, lower id first on ties."""
+    return np.lexsort((np.arange(row.size), -row.astype(np.float64)))
+
+
+def test_stress_recipe():
+    # near-flat and peaked rows as stated, with exact ties planted at ranks 0 (flat rows only),
+    # floor(k/2) and k-1; the rank k-1 pair straddles the k-th place
     s = synth.spec("stress", B=2)
+    x = synth.make_inputs(s)
+    k = s.k
+    for b in range(2):
+        for p in range(s.L):
+            row = x.logits[b, p].astype(np.float64)
+            order = _order(row)
+            flat = (b * s.L + p) % 2 == 0
+            if flat:
+                assert np.abs(row).max() < 1.0   # N(0, 0.1^2): no planted outliers
+                assert row[order[0]] == row[order[1]]   # the copied maximum
+            else:
+                assert row[order[0]] > 11.0 and row[order[1]] < 1.0   # one token +12
+            assert row[order[k // 2]] in (row[order[k // 2 - 1]], row[order[k // 2 + 1]])
+            # the k-th and (k+1)-th place hold equal values: the tie straddles the boundary
+            assert row[order[k - 1]] == row[order[k]], (b, p)
+            assert order[k - 1] < order[k]
+
+
+def test_stress_ties_straddle_both_ways():
+    # across rows the planted copy at the k-th place lands on either side of the original
+    # token's id: a copy with the lower id displaces the original from the top k, one with the
+    # higher id stays just outside it. The copies are the tokens that differ from the unplanted
+    # base row (same seeded streams, before any tie is planted).
+    s = synth.spec("stress", B=8)
+    x = synth.make_inputs(s)
+    displaced = kept = 0
+    for b in range(s.B):
+        sb = synth.sequence_seed(s.seed, b)
+        base = synth.normal(sb, synth.S_LOGITS, s.L * s.V, std=0.1).reshape(s.L, s.V)
+        peak = synth.index(sb, synth.S_BOOST_IDS, s.L, s.V)
+        for p in range(s.L):
+            row = x.logits[b, p]
+            if (b * s.L + p) % 2:
+                base[p, peak[p]] += np.float32(12.0)
+            copies = set(np.nonzero(row != base[p])[0].tolist())
+            order = _order(row)
+            pair = {int(order[s.k - 1]), int(order[s.k])}
+            copy = pair & copies
+            assert len(copy) == 1, (b, p)   # one of the straddling pair is a planted copy
+            if copy == {int(order[s.k - 1])}:
+                displaced += 1
+            else:
+                kept += 1
+    assert displaced > 0 and kept > 0
+
+
+def test_ladder_planted_ties():
+    s = synth.spec("stress", B=2, recipe="ladder")
     x = synth.make_inputs(s)
     k = s.k
     for b in range(2):
