@@ -40,6 +40,9 @@ _lib.dflash2_workspace_bytes.restype = _sz
 _lib.dflash2_select.argtypes = [_vp, _ci, _vp, _ci, _vp, _vp, _vp, _ci, _vp] + [_ci] * 6 + \
     [_vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.dflash2_select.restype = _ci
+_lib.dflash2_select_noalloc.argtypes = [_vp, _ci, _vp, _ci, _vp, _vp, _vp, _ci, _vp] + \
+    [_ci] * 6 + [_vp, _vp, _vp, _vp, _vp]
+_lib.dflash2_select_noalloc.restype = _ci
 _lib.dflash2_topk_lse_workspace_bytes.argtypes = [_ci] * 4
 _lib.dflash2_topk_lse_workspace_bytes.restype = _sz
 _lib.dflash2_topk_lse.argtypes = [_vp, _ci, _ci, _ci, _ci, _vp, _vp, _vp, _vp, _sz, _vp]
@@ -66,7 +69,7 @@ _lib.dflash2_lmhead_topk.argtypes = [_vp, _vp] + [_ci] * 4 + [_vp, _vp, _vp, _vp
 _lib.dflash2_lmhead_topk.restype = _ci
 
 EXPORTS = ("dflash2_version", "dflash2_status_string", "dflash2_workspace_bytes",
-           "dflash2_select", "dflash2_topk_lse_workspace_bytes", "dflash2_topk_lse",
+           "dflash2_select", "dflash2_select_noalloc", "dflash2_topk_lse_workspace_bytes", "dflash2_topk_lse",
            "dflash2_gate_workspace_bytes", "dflash2_gate", "dflash2_lattice", "dflash2_walk",
            "dflash2_select_ex", "dflash2_walk_ex", "dflash2_dynconv",
            "dflash2_lmhead_topk_workspace_bytes", "dflash2_lmhead_topk")
@@ -156,6 +159,34 @@ def select(logits: torch.Tensor, hidden: torch.Tensor, W_sel: torch.Tensor,
                              _ptr(edges), _ptr(path), _ptr(workspace), workspace.numel(),
                              _stream(dev))
     _check(rc, "dflash2_select")
+    return cand_ids, unary, edges, path
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def select_noalloc(logits: torch.Tensor, hidden: torch.Tensor, W_sel: torch.Tensor,
+                   pred_cb: torch.Tensor, succ_cb: torch.Tensor, anchor_ids: torch.Tensor, k: int,
+                   out: tuple):
+    """dflash2_select_noalloc: the whole selector on the library's per-GPU scratch array instead
+    of a workspace. `out` = (cand_ids, unary, edges, path), preallocated as for select()."""
+    _contig(logits, hidden, W_sel, pred_cb, succ_cb, anchor_ids)
+    B, L, V = logits.shape
+    H = hidden.shape[-1]
+    r = W_sel.shape[1]
+    if hidden.shape != (B, L, H) or W_sel.shape != (H, r) or pred_cb.shape != (V, r) \
+            or succ_cb.shape != (V, r) or anchor_ids.shape != (B,):
+        raise ValueError("inconsistent shapes")
+    if hidden.dtype != W_sel.dtype or pred_cb.dtype != succ_cb.dtype:
+        raise TypeError("hidden/W_sel and pred_cb/succ_cb must share a dtype")
+    if anchor_ids.dtype != torch.int32:
+        raise TypeError("anchor_ids must be int32")
+    cand_ids, unary, edges, path = out
+    rc = _lib.dflash2_select_noalloc(_ptr(logits), _dtype(logits), _ptr(hidden), _dtype(hidden),
+                                     _ptr(W_sel), _ptr(pred_cb), _ptr(succ_cb), _dtype(pred_cb),
+                                     _ptr(anchor_ids), B, L, V, H, r, k, _ptr(cand_ids),
+                                     _ptr(unary), _ptr(edges), _ptr(path), _stream(logits.device))
+    _check(rc, "dflash2_select_noalloc")
     return cand_ids, unary, edges, path
 
 

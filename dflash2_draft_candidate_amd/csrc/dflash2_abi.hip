@@ -5,6 +5,8 @@
 #include <float.h>
 #include <limits.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 namespace {
@@ -55,6 +57,54 @@ SelectLayout select_layout(int R, int V, int H, int r, int logits_dtype, int act
     off += round_up(topk_workspace_bytes(plan_topk(R, V, logits_dtype == DFLASH2_F32 ? 4 : 2), R));
     s.total = off;
     return s;
+}
+
+// Host-side validation of dflash2_select_ex's arguments other than the workspace.
+int check_select(const void *logits, int logits_dtype, const void *hidden, int act_dtype,
+                 const void *W_sel, const void *pred_cb, const void *succ_cb, int cb_dtype,
+                 const int32_t *anchor_ids, int B, int L, int V, int H, int r, int k,
+                 float temperature, const float *uniforms, float p_min, const int32_t *cand_ids,
+                 const float *unary, const float *edges, const int32_t *path,
+                 const int32_t *draft_len) {
+    if (B < 1 || L < 1 || H < 1 || r < 1 || r > DFLASH2_MAX_R || rows_of(B, L) > INT_MAX)
+        return DFLASH2_ERR_INVALID_ARG;
+    int rc = check_rows((int)rows_of(B, L), V, k);
+    if (rc) return rc;
+    if (!dtype_ok(logits_dtype) || !dtype_ok(act_dtype) || !dtype_ok(cb_dtype))
+        return DFLASH2_ERR_INVALID_ARG;
+    if ((rc = check_ptrs({logits, hidden, W_sel, pred_cb, succ_cb, anchor_ids, cand_ids, unary,
+                          edges, path})))
+        return rc;
+    if (!(temperature >= 0.f) || !(temperature <= FLT_MAX) || p_min != p_min ||
+        (temperature > 0.f && !uniforms))
+        return DFLASH2_ERR_INVALID_ARG;
+    if ((uniforms && !aligned16(uniforms)) || (draft_len && !aligned16(draft_len)))
+        return DFLASH2_ERR_ALIGNMENT;
+    return DFLASH2_OK;
+}
+
+// The allocation-free entry point's workspace: one array per GPU, part of the loaded code object.
+// In host code `scratch` names a host-side stand-in, not device memory: only the address that
+// hipGetSymbolAddress returns for the current device is ever passed on.
+static __device__ __align__(256) unsigned char scratch[DFLASH2_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];  // device address of each GPU's array, once found
+
+// The current device's scratch array (found on the first call with that device current).
+int current_scratch(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DFLASH2_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return DFLASH2_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DFLASH2_OK;
 }
 
 }  // namespace
@@ -215,21 +265,11 @@ int dflash2_select_ex(const void *logits, int logits_dtype, const void *hidden, 
                       float temperature, const float *uniforms, float p_min, int32_t *cand_ids,
                       float *unary, float *edges, int32_t *path, int32_t *draft_len,
                       void *workspace, size_t workspace_bytes, void *stream) {
-    if (B < 1 || L < 1 || H < 1 || r < 1 || r > DFLASH2_MAX_R || rows_of(B, L) > INT_MAX)
-        return DFLASH2_ERR_INVALID_ARG;
-    const int R = (int)rows_of(B, L);
-    int rc = check_rows(R, V, k);
+    int rc = check_select(logits, logits_dtype, hidden, act_dtype, W_sel, pred_cb, succ_cb,
+                          cb_dtype, anchor_ids, B, L, V, H, r, k, temperature, uniforms, p_min,
+                          cand_ids, unary, edges, path, draft_len);
     if (rc) return rc;
-    if (!dtype_ok(logits_dtype) || !dtype_ok(act_dtype) || !dtype_ok(cb_dtype))
-        return DFLASH2_ERR_INVALID_ARG;
-    if ((rc = check_ptrs({logits, hidden, W_sel, pred_cb, succ_cb, anchor_ids, cand_ids, unary,
-                          edges, path})))
-        return rc;
-    if (!(temperature >= 0.f) || !(temperature <= FLT_MAX) || p_min != p_min ||
-        (temperature > 0.f && !uniforms))
-        return DFLASH2_ERR_INVALID_ARG;
-    if ((uniforms && !aligned16(uniforms)) || (draft_len && !aligned16(draft_len)))
-        return DFLASH2_ERR_ALIGNMENT;
+    const int R = (int)rows_of(B, L);
     const size_t need = dflash2_workspace_bytes(B, L, V, H, r, k);
     if (!workspace || workspace_bytes < need) return DFLASH2_ERR_WORKSPACE;
     if (!aligned16(workspace)) return DFLASH2_ERR_ALIGNMENT;
@@ -281,6 +321,26 @@ int dflash2_select(const void *logits, int logits_dtype, const void *hidden, int
     return dflash2_select_ex(logits, logits_dtype, hidden, act_dtype, W_sel, pred_cb, succ_cb,
                              cb_dtype, anchor_ids, B, L, V, H, r, k, 0.f, nullptr, 0.f, cand_ids,
                              unary, edges, path, nullptr, workspace, workspace_bytes, stream);
+}
+
+int dflash2_select_noalloc(const void *logits, int logits_dtype, const void *hidden,
+                           int act_dtype, const void *W_sel, const void *pred_cb,
+                           const void *succ_cb, int cb_dtype, const int32_t *anchor_ids, int B,
+                           int L, int V, int H, int r, int k, int32_t *cand_ids, float *unary,
+                           float *edges, int32_t *path, void *stream) {
+    // every argument is checked before the array is looked up
+    int rc = check_select(logits, logits_dtype, hidden, act_dtype, W_sel, pred_cb, succ_cb,
+                          cb_dtype, anchor_ids, B, L, V, H, r, k, 0.f, nullptr, 0.f, cand_ids,
+                          unary, edges, path, nullptr);
+    if (rc) return rc;
+    if (dflash2_workspace_bytes(B, L, V, H, r, k) > DFLASH2_NOALLOC_SCRATCH_BYTES)
+        return DFLASH2_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if ((rc = current_scratch(&ws)) != DFLASH2_OK) return rc;
+    return dflash2_select_ex(logits, logits_dtype, hidden, act_dtype, W_sel, pred_cb, succ_cb,
+                             cb_dtype, anchor_ids, B, L, V, H, r, k, 0.f, nullptr, 0.f, cand_ids,
+                             unary, edges, path, nullptr, ws, DFLASH2_NOALLOC_SCRATCH_BYTES,
+                             stream);
 }
 
 }  // extern "C"

@@ -106,6 +106,29 @@ int dflash2_select(const void *logits, int logits_dtype, const void *hidden, int
                    size_t workspace_bytes, void *stream);
 
 /*
+ * dflash2_select_noalloc - dflash2_select for callers that cannot allocate device memory (code
+ *   under HIP graph capture, tight serving loops, harnesses that forbid allocation). Same
+ *   arguments, outputs and errors as dflash2_select, without the workspace: the library's own
+ *   scratch array of DFLASH2_NOALLOC_SCRATCH_BYTES bytes per GPU serves as the workspace. The
+ *   call allocates nothing. The array belongs to the device current at the call (the stream must
+ *   be one of that device's); it is found once per device, on the first call made with that
+ *   device current, and is held until the process ends.
+ *   - A call whose dflash2_workspace_bytes(B, L, V, H, r, k) exceeds
+ *     DFLASH2_NOALLOC_SCRATCH_BYTES returns DFLASH2_ERR_WORKSPACE before anything is launched.
+ *   - Every call on one GPU shares that GPU's array and leaves its contents behind; nothing in
+ *     it needs clearing between calls. Calls that overlap on one GPU (several streams or host
+ *     threads) race on the array: the caller must order them.
+ *   - Failing to find the array's device address returns DFLASH2_ERR_HIP.
+ */
+#define DFLASH2_NOALLOC_SCRATCH_BYTES (16u << 20) /* 16 MiB per GPU */
+
+int dflash2_select_noalloc(const void *logits, int logits_dtype, const void *hidden,
+                           int act_dtype, const void *W_sel, const void *pred_cb,
+                           const void *succ_cb, int cb_dtype, const int32_t *anchor_ids, int B,
+                           int L, int V, int H, int r, int k, int32_t *cand_ids, float *unary,
+                           float *edges, int32_t *path, void *stream);
+
+/*
  * dflash2_select_ex - dflash2_select with the walk's two further modes (dflash2_select is this
  *   call with temperature = 0, uniforms = NULL, p_min = 0, draft_len = NULL). Same arguments,
  *   workspace and outputs, plus:

@@ -23,11 +23,12 @@ MIS = 0x100008        # fake, misaligned
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        from dflash2_draft_candidate_amd import build as b
-        b.build()
+        import __graft_entry__
+        __graft_entry__._hip_build_module().build()
     L = ctypes.CDLL(LIB)
     vp, ci, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     L.dflash2_select.argtypes = [vp, ci, vp, ci, vp, vp, vp, ci, vp] + [ci] * 6 + [vp] * 5 + [sz, vp]
+    L.dflash2_select_noalloc.argtypes = [vp, ci, vp, ci, vp, vp, vp, ci, vp] + [ci] * 6 + [vp] * 5
     L.dflash2_workspace_bytes.argtypes = [ci] * 6
     L.dflash2_workspace_bytes.restype = sz
     L.dflash2_topk_lse.argtypes = [vp, ci, ci, ci, ci, vp, vp, vp, vp, sz, vp]
@@ -62,6 +63,7 @@ def test_header_declares_the_abi():
     for f in ("dflash2_select", "dflash2_workspace_bytes", "dflash2_status_string",
               "dflash2_topk_lse", "dflash2_gate", "dflash2_lattice", "dflash2_walk",
               "dflash2_select_ex", "dflash2_walk_ex", "dflash2_dynconv", "dflash2_lmhead_topk",
+              "dflash2_select_noalloc",
               "dflash2_lmhead_topk_workspace_bytes"):
         assert f in names
 
@@ -193,3 +195,33 @@ def test_binding_rejects_host_tensors():
     import dflash2_draft_candidate_amd as d2
     with pytest.raises(ValueError):
         d2.topk_lse(torch.zeros(2, 10), 2)
+
+
+def _noalloc(lib, B=2, L=4, V=1000, H=64, r=16, k=8, ptrs=None, dts=(BF16, BF16, BF16)):
+    p = ptrs or {}
+    g = lambda n: p.get(n, P)
+    return lib.dflash2_select_noalloc(g("logits"), dts[0], g("hidden"), dts[1], g("W"), g("pred"),
+                                      g("succ"), dts[2], g("anchor"), B, L, V, H, r, k,
+                                      g("ids"), g("unary"), g("edges"), g("path"), None)
+
+
+def test_select_noalloc_validation(lib):
+    # the same argument errors as dflash2_select, all before the scratch array is looked up
+    assert _noalloc(lib, k=0) == EINVAL
+    assert _noalloc(lib, k=65) == EINVAL
+    assert _noalloc(lib, r=257) == EINVAL
+    assert _noalloc(lib, V=4, k=8) == EINVAL
+    assert _noalloc(lib, dts=(BF16, 7, BF16)) == EINVAL
+    assert _noalloc(lib, ptrs={"edges": None}) == EINVAL
+    assert _noalloc(lib, ptrs={"hidden": MIS}) == EALIGN
+
+
+def test_select_noalloc_size_limit(lib):
+    # more than DFLASH2_NOALLOC_SCRATCH_BYTES of workspace: refused before anything runs
+    limit = 16 << 20
+    big = (2048, 16, 262144, 8192, 256, 64)
+    assert lib.dflash2_workspace_bytes(*big) > limit
+    B, L, V, H, r, k = big
+    assert _noalloc(lib, B, L, V, H, r, k) == EWS
+    serving = (64, 16, 151936, 4096, 64, 16)
+    assert lib.dflash2_workspace_bytes(*serving) <= limit
