@@ -411,6 +411,58 @@ def summarize(a: list[str]):
             f"| traffic / algorithmic | {(fetch_b + write_b) / k1_bytes(s):.4f} |\n")
         print(TRAFFIC_FILE, md)
         return
+    if a[0] == "counters":
+        import synth
+        csv_paths, out_md, workload, cmd = a[1].split(","), a[2], a[3], a[4]
+        s = synth.spec(workload)
+        rows = []
+        for path in csv_paths:
+            rows += list(csv.DictReader(open(path)))
+        per = {}   # kernel -> counter -> values (one per dispatch)
+        for r in rows:
+            k = _kernel_name(r["Kernel_Name"])
+            if "copyBuffer" in k or "fill" in k.lower() or "elementwise" in k.lower():
+                continue
+            per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+        names = sorted({c for v in per.values() for c in v})
+        lines = [f"# Counters: {os.path.basename(out_md)[:-3]}", "",
+                 "rocprofv3 counter passes, one run per pass (from the repository root on a "
+                 "one-GPU MI355X box):", ""]
+        lines += [f"    {c}" for c in cmd.split(" ;; ")]
+        lines += ["", f"Workload {workload}: R = {s.R} rows of V = {s.V} ({s.logits_dtype}).",
+                  "Values are means per dispatch over the profiled launches; SQ instruction "
+                  "counts are wave instructions summed over the chip, SQ_ACTIVE_INST_VALU and "
+                  "SQ_VALU_MFMA_BUSY_CYCLES are summed over the SIMDs.", "",
+                  "| kernel | " + " | ".join(names) + " |",
+                  "|---|" + "---|" * len(names)]
+        for k, cs in sorted(per.items()):
+            vals = [f"{sum(cs[n]) / len(cs[n]):.4g}" if n in cs else "" for n in names]
+            lines.append(f"| `{k}` | " + " | ".join(vals) + " |")
+        elems = s.R * s.V
+        derived = []
+        for k, cs in sorted(per.items()):
+            m = lambda n: sum(cs[n]) / len(cs[n]) if n in cs else None
+            if "topk_lse_kernel" in k and m("SQ_INSTS_VALU"):
+                derived.append(f"| `{k}` | VALU instructions per element | "
+                               f"{m('SQ_INSTS_VALU') * 64 / elems:.3f} |")
+                if m("SQ_INSTS_VALU_TRANS_F32"):
+                    derived.append(f"| `{k}` | transcendental instructions per element | "
+                                   f"{m('SQ_INSTS_VALU_TRANS_F32') * 64 / elems:.3f} |")
+                if m("SQ_ACTIVE_INST_VALU"):
+                    derived.append(f"| `{k}` | VALU issue quad-cycles per VALU instruction | "
+                                   f"{m('SQ_ACTIVE_INST_VALU') / m('SQ_INSTS_VALU'):.3f} |")
+            if m("SQ_INSTS_VALU_MFMA_MOPS_BF16"):
+                derived.append(f"| `{k}` | bf16 MFMA flops per dispatch (MOPS x 512) | "
+                               f"{m('SQ_INSTS_VALU_MFMA_MOPS_BF16') * 512:.4g} |")
+            if m("TCC_HIT_sum") is not None and m("TCC_MISS_sum"):
+                h, mi = m("TCC_HIT_sum"), m("TCC_MISS_sum")
+                derived.append(f"| `{k}` | L2 hit rate | {h / (h + mi):.3f} |")
+        if derived:
+            lines += ["", "| kernel | derived | value |", "|---|---|---|"] + derived
+        open(out_md, "w").write("\n".join(lines) + "\n")
+        print(out_md)
+        return
     raise SystemExit(f"unknown summary kind {a[0]}")
 
 
@@ -428,8 +480,9 @@ def main():
                     help="with --k1-only: also run device-to-device copies of this many MiB, the "
                          "calibration for the HBM byte counters")
     ap.add_argument("--summarize", nargs="+", metavar="ARG",
-                    help="no GPU: 'trace STATS_CSV OUT_MD CMD' or 'traffic FETCH_CSV WRITE_CSV "
-                         "WORKLOAD CMD' writes a profiles/ summary from rocprofv3 output")
+                    help="no GPU: 'trace STATS_CSV OUT_MD CMD', 'traffic FETCH_CSV WRITE_CSV "
+                         "WORKLOAD CMD' or 'counters CSV[,CSV...] OUT_MD WORKLOAD CMDS' writes a "
+                         "profiles/ summary from rocprofv3 output (CMDS: commands joined by ' ;; ')")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize)
