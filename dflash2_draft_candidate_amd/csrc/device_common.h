@@ -74,37 +74,96 @@ __device__ __forceinline__ int32_t key_id(uint64_t key) {
 
 __device__ __forceinline__ float key_logit(uint64_t key) { return key_value((uint32_t)(key >> 32)); }
 
+// ---- lane exchanges in the VALU (no LDS round trip) ------------------------------------------
+// Lane l receives lane l ^ S. Within a row of 16 lanes: DPP quad permutations (S = 1, 2), the row
+// rotations by 12 and 4 (row_ror:n reads lane (l - n) mod 16; S = 4 takes l + 4 or l - 4 by lane
+// bit 2) and by 8 (S = 8). Across rows, gfx950's permlane swaps on two copies of the value:
+// permlane16_swap(v, v) returns the even rows of v in both rows of each pair, then the odd rows;
+// permlane32_swap(v, v) the low half of the wave in both halves, then the high half.
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowRor12 = 0x12C;
+constexpr int kDppRowMirror = 0x140;  // lane l reads lane 15 - l of its row
+
+template <int S>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane) {
+    static_assert(S == 1 || S == 2 || S == 4 || S == 8 || S == 16 || S == 32, "lane xor");
+    if constexpr (S == 1)
+        return __builtin_amdgcn_update_dpp(0u, v, kDppQuadXor1, 0xF, 0xF, false);
+    if constexpr (S == 2)
+        return __builtin_amdgcn_update_dpp(0u, v, kDppQuadXor2, 0xF, 0xF, false);
+    if constexpr (S == 4) {
+        const uint32_t up = __builtin_amdgcn_update_dpp(0u, v, kDppRowRor12, 0xF, 0xF, false);
+        const uint32_t dn = __builtin_amdgcn_update_dpp(0u, v, kDppRowRor4, 0xF, 0xF, false);
+        return (lane & 4) ? dn : up;
+    }
+    if constexpr (S == 8)
+        return __builtin_amdgcn_update_dpp(0u, v, kDppRowRor8, 0xF, 0xF, false);
+    if constexpr (S == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16) ? r[0] : r[1];
+    }
+    if constexpr (S == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane & 32) ? r[0] : r[1];
+    }
+}
+
+template <int S>
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v, int lane) {
+    const uint32_t lo = xor_lane<S>((uint32_t)v, lane);
+    const uint32_t hi = xor_lane<S>((uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Lane l receives lane 63 - l: the row mirror (l ^ 15 within a row), then l ^ 16 and l ^ 32.
+__device__ __forceinline__ uint64_t reverse_lanes64(uint64_t v, int lane) {
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, kDppRowMirror, 0xF, 0xF, false);
+    const uint32_t hi =
+        __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), kDppRowMirror, 0xF, 0xF, false);
+    return xor_lane64<32>(xor_lane64<16>(((uint64_t)hi << 32) | lo, lane), lane);
+}
+
 // ---- wave-wide sorting networks on 64-bit keys (one key per lane, lane 0 = largest) --------
 
 __device__ __forceinline__ uint64_t kmax(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t kmin(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
+// One compare-exchange step with the partner l ^ S: the lower lane of the pair keeps the
+// larger key when `desc`, the smaller otherwise.
+template <int S>
+__device__ __forceinline__ uint64_t bitonic_step(uint64_t key, int lane, bool desc) {
+    const uint64_t other = xor_lane64<S>(key, lane);
+    const bool lower = (lane & S) == 0;
+    return (lower == desc) ? kmax(key, other) : kmin(key, other);
+}
+
+// Compare-exchange steps with the partners l ^ S, l ^ S/2, ..., l ^ 1 (one bitonic merge).
+template <int S>
+__device__ __forceinline__ uint64_t bitonic_merge_steps(uint64_t key, int lane, bool desc) {
+    key = bitonic_step<S>(key, lane, desc);
+    if constexpr (S > 1) key = bitonic_merge_steps<S / 2>(key, lane, desc);
+    return key;
+}
+
 // Bitonic sort of the 64 lane keys into descending lane order.
 __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key, int lane) {
-#pragma unroll
-    for (int size = 2; size <= kWave; size <<= 1) {
-#pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const uint64_t other = __shfl_xor(key, stride, kWave);
-            const bool desc = (lane & size) == 0;
-            const bool lower = (lane & stride) == 0;
-            key = (lower == desc) ? kmax(key, other) : kmin(key, other);
-        }
-    }
+    key = bitonic_merge_steps<1>(key, lane, (lane & 2) == 0);
+    key = bitonic_merge_steps<2>(key, lane, (lane & 4) == 0);
+    key = bitonic_merge_steps<4>(key, lane, (lane & 8) == 0);
+    key = bitonic_merge_steps<8>(key, lane, (lane & 16) == 0);
+    key = bitonic_merge_steps<16>(key, lane, (lane & 32) == 0);
+    key = bitonic_merge_steps<32>(key, lane, true);
     return key;
 }
 
 // a and c are each sorted descending across the lanes; returns the 64 largest keys of both,
 // sorted descending (bitonic merge).
 __device__ __forceinline__ uint64_t wave_merge_desc(uint64_t a, uint64_t c, int lane) {
-    const uint64_t c_rev = __shfl(c, kWave - 1 - lane, kWave);
-    uint64_t m = kmax(a, c_rev);
-#pragma unroll
-    for (int stride = kWave / 2; stride > 0; stride >>= 1) {
-        const uint64_t other = __shfl_xor(m, stride, kWave);
-        m = ((lane & stride) == 0) ? kmax(m, other) : kmin(m, other);
-    }
-    return m;
+    const uint64_t m = kmax(a, reverse_lanes64(c, lane));
+    return bitonic_merge_steps<32>(m, lane, true);
 }
 
 // ---- cross-lane reductions (DPP: no LDS round trip) -----------------------------------------
