@@ -54,7 +54,7 @@ SelectLayout select_layout(int R, int V, int H, int r, int logits_dtype, int act
     s.gpart = off;
     off += round_up((size_t)gate_splits(R, H, act_dtype) * R * r * sizeof(float));
     s.topk = off;
-    off += round_up(topk_workspace_bytes(plan_topk(R, V, logits_dtype == DFLASH2_F32 ? 4 : 2), R));
+    off += round_up(topk_pass_workspace_bytes(R, V, logits_dtype == DFLASH2_F32 ? 4 : 2));
     s.total = off;
     return s;
 }
@@ -127,7 +127,7 @@ const char *dflash2_status_string(int status) {
 
 size_t dflash2_topk_lse_workspace_bytes(int R, int V, int k, int logits_dtype) {
     if (check_rows(R, V, k) != DFLASH2_OK || !dtype_ok(logits_dtype)) return 0;
-    return topk_workspace_bytes(plan_topk(R, V, logits_dtype == DFLASH2_F32 ? 4 : 2), R);
+    return topk_pass_workspace_bytes(R, V, logits_dtype == DFLASH2_F32 ? 4 : 2);
 }
 
 int dflash2_topk_lse(const void *logits, int logits_dtype, int R, int V, int k, int32_t *cand_ids,

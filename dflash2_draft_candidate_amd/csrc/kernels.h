@@ -27,9 +27,27 @@ struct FusedGate {
 };
 // Splits of the fused gate for these sizes; 0 if the pass cannot carry the gate (r > 128).
 int fused_gate_splits(int R, int V, int logits_dtype, int H, int r);
+// Workspace of the top-k pass for these sizes (whichever kernel launch_topk_lse picks).
+size_t topk_pass_workspace_bytes(int R, int V, int elem_bytes);
 hipError_t launch_topk_lse(const void *logits, int logits_dtype, int R, int V, int k,
                            int32_t *cand_ids, float *unary, float *lse, void *workspace,
                            hipStream_t stream, const FusedGate *gate = nullptr);
+
+// The top-k pass for rows too few to fill the chip (topk_small.hip): `slices` workgroups per
+// row, one load round each, slices merged in the kernel through per-row arrival counters.
+struct SmallPlanInfo {
+    int slices;
+};
+bool plan_small(int R, int V, int elem_bytes, SmallPlanInfo &plan);
+size_t small_workspace_bytes(const SmallPlanInfo &plan, int R);
+int small_gate_nt(int r);  // gate tile width it carries for rank r (0: r too large)
+hipError_t launch_topk_small(const SmallPlanInfo &plan, const void *logits, int logits_dtype,
+                             int R, int V, int k, uint32_t epoch, int32_t *cand_ids, float *unary,
+                             float *lse, void *workspace, hipStream_t stream,
+                             const FusedGate *gate);
+// The arrival counters' epoch for one launch: a process-wide launch count (never 0), so epochs grow
+// from launch to launch until the count wraps.
+uint32_t next_launch_epoch();
 
 // ---- K2: gate GEMM ---------------------------------------------------------------------------
 // bf16 runs as `gate_splits` partial products over ranges of H, [splits][R][r] floats;

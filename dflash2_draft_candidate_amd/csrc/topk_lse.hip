@@ -51,9 +51,12 @@
 //     other twelve waves absorb the delay. A gate rides along only where its tile parts fit in
 //     LDS beside the chunk sums of the pass's own plan (so select and the stage-by-stage calls
 //     sum the same chunks). Tiles are numbered XCD by XCD (see xcd_major).
+#include <atomic>
+
 #include "device_common.h"
 #include "gate_tile.h"
 #include "kernels.h"
+#include "row_slices.h"
 
 namespace dflash2 {
 namespace {
@@ -451,45 +454,6 @@ __device__ __forceinline__ void batch(const u32x4 *buf, int nvalid, int32_t id_b
         hits = __ballot(bmax != -INFINITY && bmax >= w.tau_v);
     }
     offer_lanes<T, kU, (NB < kWave ? NB : kWave)>(w, buf, hits, nvalid, id_base, EV, lane, stage);
-}
-
-// Whole vectors of a unit and its ragged row ends (elements outside whole vectors: the first
-// slice takes the head, the last slice the tail).
-struct UnitRange {
-    int64_t g0;      // first element of the row
-    int64_t c0;      // first whole vector of the unit
-    int nv;          // whole vectors of the unit
-    int64_t h0, h1;  // ragged head [h0, h1)
-    int64_t t0, t1;  // ragged tail [t0, t1)
-};
-
-// floor(n * s / S) for n < 2^31 and s <= S < 2^16, in 32-bit arithmetic (n = a S + b gives
-// a s + floor(b s / S)); 64-bit divisions cost hundreds of scalar instructions.
-__device__ __forceinline__ int64_t split_point(uint32_t n, uint32_t s, uint32_t S) {
-    return (int64_t)(n / S) * s + (n % S) * s / S;
-}
-
-__device__ __forceinline__ UnitRange unit_range(int64_t unit, int V, int S, int EV) {
-    UnitRange u;
-    const uint32_t row = (uint32_t)unit / (uint32_t)S;  // units and slices fit in 31 bits
-    const uint32_t slice = (uint32_t)unit - row * (uint32_t)S;
-    u.g0 = (int64_t)row * V;
-    const int64_t g1 = u.g0 + V;
-    int64_t va = (u.g0 + EV - 1) / EV, vb = g1 / EV;
-    if (va > vb) va = vb = 0;  // the row lies inside one vector: all of it is ragged
-    const uint32_t nvec = (uint32_t)(vb - va);
-    u.c0 = va + split_point(nvec, slice, (uint32_t)S);
-    u.nv = (int)(va + split_point(nvec, slice + 1, (uint32_t)S) - u.c0);
-    u.h0 = u.h1 = u.t0 = u.t1 = 0;
-    if (slice == 0) {
-        u.h0 = u.g0;
-        u.h1 = nvec > 0 ? va * EV : g1;
-    }
-    if (slice == S - 1 && nvec > 0) {
-        u.t0 = vb * EV;
-        u.t1 = g1;
-    }
-    return u;
 }
 
 // Unit q and index wv within the unit of wave slot s, mixing the SIMD age classes (slot s sits
@@ -1086,7 +1050,22 @@ size_t topk_workspace_bytes(const TopkPlan &p, int R) {
     return (size_t)R * p.slices * (kWave * sizeof(uint64_t) + sizeof(float2));
 }
 
+uint32_t next_launch_epoch() {
+    static std::atomic<uint32_t> launches{0};
+    uint32_t e = launches.fetch_add(1, std::memory_order_relaxed) + 1u;
+    return e == 0u ? 1u : e;  // after 2^32 launches it wraps (the kernel then re-bases by CAS)
+}
+
+size_t topk_pass_workspace_bytes(int R, int V, int elem_bytes) {
+    SmallPlanInfo sp;
+    if (plan_small(R, V, elem_bytes, sp)) return small_workspace_bytes(sp, R);
+    return topk_workspace_bytes(plan_topk(R, V, elem_bytes), R);
+}
+
 int fused_gate_splits(int R, int V, int logits_dtype, int H, int r) {
+    SmallPlanInfo sp;
+    if (plan_small(R, V, logits_dtype == 0 ? 4 : 2, sp))
+        return small_gate_nt(r) ? gate_splits(R, H, 1) : 0;  // gate tiles as extra workgroups
     const int nt = fused_gate_nt(r);
     if (nt == 0) return 0;
     // The plan (its chunks above all) is the one the pass has without a gate, so both give the
@@ -1104,6 +1083,10 @@ int fused_gate_splits(int R, int V, int logits_dtype, int H, int r) {
 hipError_t launch_topk_lse(const void *logits, int logits_dtype, int R, int V, int k,
                            int32_t *cand_ids, float *unary, float *lse, void *workspace,
                            hipStream_t stream, const FusedGate *gate) {
+    SmallPlanInfo sp;
+    if (plan_small(R, V, logits_dtype == 0 ? 4 : 2, sp))
+        return launch_topk_small(sp, logits, logits_dtype, R, V, k, next_launch_epoch(), cand_ids,
+                                 unary, lse, workspace, stream, gate);
     const int nt = gate ? fused_gate_nt(gate->r) : 0;
     if (gate && nt == 0) return hipErrorInvalidValue;
     const TopkPlan plan = plan_topk(R, V, logits_dtype == 0 ? 4 : 2);
