@@ -15,8 +15,12 @@ Prints one JSON line:
                comes from committed rocprofv3 counter readings when they match the current kernel
   cpu_baseline the fp64 C oracle on the host, on the same workload: row-parallel over the host's
                cores (value, cores) and single-threaded (single_thread), with the CPU model
-  per_config   end-to-end latency and K1 bandwidth of every workload
-  extras       the default workload with the walk's sampling and p_min modes, the grouped
+  per_config   end-to-end latency and K1 bandwidth of every workload (eager launches; `graph`:
+               the same calls captured in a HIP graph and replayed, the GPU side without the
+               host's per-call launch cost)
+  extras       the default workload with the walk's sampling and p_min modes, its gate product
+               alone (dflash2_gate: flops against the bf16 matrix-core peak, bytes against HBM),
+               the grouped
                dynamic depthwise convolution at the serving block shape, and the LM-head product
                with the top-k pass folded in (16 rows, V = 151936, H = 4096), against its HBM
                roofline, beside a library product followed by the top-k pass
@@ -35,9 +39,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "selector positions/sec and top-k pass HBM GB/s (% of peak) at V=151936, L=16, k=16"
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 matrix cores
 POOL_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "topk_lse_traffic.json")
-K1_SOURCE = os.path.join(ROOT, "dflash2_draft_candidate_amd", "csrc", "topk_lse.hip")
+# the sources the streaming top-k kernel is compiled from (the traffic readings name their hash)
+K1_SOURCES = [os.path.join(ROOT, "dflash2_draft_candidate_amd", "csrc", f)
+              for f in ("topk_lse.hip", "row_slices.h", "device_common.h", "gate_tile.h")]
 K1_KERNEL = "topk_lse_kernel"
 COPY_KERNEL = "copyBuffer"  # the HIP runtime's device-to-device copy kernel
 COPY_REPS = 5
@@ -53,8 +60,11 @@ def k1_bytes(s) -> int:
     return s.R * (s.V * elem + s.k * 8 + 4)
 
 
-def source_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_hash(paths: list[str]) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
 class Workload:
@@ -143,6 +153,35 @@ def time_loop(fn, steps: int, warmup: int, warm_seconds: float = WARM_SECONDS,
     return total / steps
 
 
+def graph_loop(fn, n: int, replays: int, warm_seconds: float = WARM_SECONDS) -> float:
+    """Mean milliseconds per call of fn(j) when calls j = 0 .. n-1 are captured once in a HIP
+    graph and the graph is replayed `replays` times (HIP events around the replays, after
+    warm_seconds of untimed replays): the GPU side of the step without the host's per-call
+    launch cost, which bounds the eager loop at small sizes."""
+    import torch
+    for j in range(n):
+        fn(j)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for j in range(n):
+            fn(j)
+    t0 = time.time()
+    while time.time() - t0 < warm_seconds:
+        g.replay()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (replays * n)
+
+
+GRAPH_CALLS = 32  # calls per captured graph (over distinct pool copies)
+
+
 def measure(name: str, device: str, steps: int, warmup: int) -> dict:
     import torch
     w = Workload(name, device)
@@ -160,11 +199,18 @@ def measure(name: str, device: str, steps: int, warmup: int) -> dict:
     k1_ms = time_loop(lambda i: w.k1_step(i, ids, unary, lse, ws), steps, warmup,
                       stats=k1_stats)
     gbs = k1_bytes(s) / (k1_ms * 1e-3) / 1e9
+    n_graph = min(GRAPH_CALLS, len(w.logits))
+    replays = max(1, steps // n_graph)
+    e2e_graph_ms = graph_loop(w.step, n_graph, replays)
+    k1_graph_ms = graph_loop(lambda i: w.k1_step(i, ids, unary, lse, ws), n_graph, replays)
     res = {"B": s.B, "L": s.L, "k": s.k, "V": s.V, "H": s.H, "r": s.r,
            "logits": s.logits_dtype, "e2e_us": round(e2e_ms * 1e3, 2),
            "positions_per_s": round(s.R / (e2e_ms * 1e-3), 1), "k1_us": round(k1_ms * 1e3, 2),
            "k1_gbs": round(gbs, 1), "k1_frac": round(gbs / PEAK_HBM_GBS, 4),
-           "e2e_us_per_step": e2e_stats, "k1_us_per_step": k1_stats}
+           "e2e_us_per_step": e2e_stats, "k1_us_per_step": k1_stats,
+           "graph": {"calls_per_graph": n_graph, "replays": replays,
+                     "e2e_us": round(e2e_graph_ms * 1e3, 2),
+                     "k1_us": round(k1_graph_ms * 1e3, 2)}}
     res["_workload"] = w
     return res
 
@@ -219,6 +265,45 @@ def measure_dynconv(device: str, steps: int, warmup: int) -> dict:
     return {"shape": {"n_blocks": nb, "T": T, "C": C, "K": K, "group": G, "dtype": "bf16"},
             "launch_us": round(ms * 1e3, 2), "algorithmic_bytes": nbytes, "gbs": round(gbs, 1),
             "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def measure_gate(w, steps: int, warmup: int) -> dict:
+    """The stand-alone gate product g = hidden . W_sel (dflash2_gate) on the workload's rows:
+    launch time over a rotating pool of hidden copies, its rate in flops (2 R H r) against the
+    dense bf16 matrix-core peak and in algorithmic bytes (hidden, W_sel, the fp32 g) against HBM;
+    with H r / (H + r) flops per byte it is bound by HBM."""
+    import ctypes
+    import torch
+    import dflash2_draft_candidate_amd as d2
+    s = w.s
+    R, H, r = s.R, s.H, s.r
+    hid = [h.reshape(R, H) for h in w.hidden]
+    g = torch.empty((R, r), dtype=torch.float32, device=hid[0].device)
+    lib = d2.library()
+    ws = torch.empty(max(16, lib.dflash2_gate_workspace_bytes(R, H, r)), dtype=torch.uint8,
+                     device=hid[0].device)
+    dt = d2._dtype(hid[0])
+
+    def step(i):
+        rc = lib.dflash2_gate(ctypes.c_void_p(hid[i % len(hid)].data_ptr()),
+                              ctypes.c_void_p(w.W.data_ptr()), dt, R, H, r,
+                              ctypes.c_void_p(g.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                              ws.numel(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"dflash2_gate failed with status {rc}")
+
+    ms = time_loop(step, steps, warmup)
+    graph_ms = graph_loop(step, min(GRAPH_CALLS, len(hid)), max(1, steps // GRAPH_CALLS))
+    el = hid[0].element_size()
+    flops = 2.0 * R * H * r
+    nbytes = R * H * el + H * r * el + R * r * 4
+    return {"shape": {"R": R, "H": H, "r": r, "dtype": s.act_dtype},
+            "launch_us": round(ms * 1e3, 2), "graph_launch_us": round(graph_ms * 1e3, 2),
+            "tflops": round(flops / (graph_ms * 1e-3) / 1e12, 2),
+            "frac_mfma_bf16": round(flops / (graph_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
+            "algorithmic_bytes": nbytes, "gbs": round(nbytes / (graph_ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nbytes / (graph_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "bound": "hbm"}
 
 
 def measure_lmhead(device: str, steps: int, warmup: int) -> dict:
@@ -323,7 +408,7 @@ def committed_traffic() -> dict | None:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if t.get("k1_source_sha256_16") != source_hash(K1_SOURCE):
+    if t.get("k1_source_sha256_16") != source_hash(K1_SOURCES):
         return None
     return t
 
@@ -382,7 +467,7 @@ def summarize(a: list[str]):
         write_b = w_k1 * 1024 / w_factor
         s = synth.spec(workload)
         t = {"kernel": K1_KERNEL, "workload": workload,
-             "k1_source_sha256_16": source_hash(K1_SOURCE),
+             "k1_source_sha256_16": source_hash(K1_SOURCES),
              "bytes_per_launch": int(round(fetch_b + write_b)),
              "fetch_bytes_per_launch": int(round(fetch_b)),
              "write_bytes_per_launch": int(round(write_b)),
@@ -443,7 +528,26 @@ def summarize(a: list[str]):
         derived = []
         for k, cs in sorted(per.items()):
             m = lambda n: sum(cs[n]) / len(cs[n]) if n in cs else None
-            if "topk_lse_kernel" in k and m("SQ_INSTS_VALU"):
+            # GRBM_GUI_ACTIVE is read on each of the 8 XCDs and summed: the dispatch's busy
+            # cycles are an eighth of it
+            busy = m("GRBM_GUI_ACTIVE") / 8 if m("GRBM_GUI_ACTIVE") else None
+            if busy:
+                derived.append(f"| `{k}` | busy cycles (GRBM_GUI_ACTIVE / 8 XCDs) | {busy:.4g} |")
+            if busy and m("SQ_ACTIVE_INST_VALU"):
+                derived.append(f"| `{k}` | VALU busy (SQ_ACTIVE_INST_VALU x 4 / 1024 SIMDs / "
+                               f"busy cycles) | {m('SQ_ACTIVE_INST_VALU') * 4 / 1024 / busy:.3f} |")
+            if busy and m("SQ_WAVE_CYCLES"):
+                derived.append(f"| `{k}` | mean resident waves per CU (SQ_WAVE_CYCLES x 4 / "
+                               f"busy cycles / 256 CUs) | "
+                               f"{m('SQ_WAVE_CYCLES') * 4 / busy / 256:.2f} |")
+            if busy and m("SQ_VALU_MFMA_BUSY_CYCLES"):
+                derived.append(f"| `{k}` | MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / "
+                               f"busy cycles) | "
+                               f"{m('SQ_VALU_MFMA_BUSY_CYCLES') / busy / 1024:.4f} |")
+            if m("SQ_LDS_IDX_ACTIVE") and m("SQ_LDS_BANK_CONFLICT") is not None:
+                derived.append(f"| `{k}` | LDS bank-conflict cycles per LDS-active cycle | "
+                               f"{m('SQ_LDS_BANK_CONFLICT') / m('SQ_LDS_IDX_ACTIVE'):.4f} |")
+            if ("topk_lse_kernel" in k or "topk_small_kernel" in k) and m("SQ_INSTS_VALU"):
                 derived.append(f"| `{k}` | VALU instructions per element | "
                                f"{m('SQ_INSTS_VALU') * 64 / elems:.3f} |")
                 if m("SQ_INSTS_VALU_TRANS_F32"):
@@ -476,6 +580,8 @@ def main():
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--k1-only", action="store_true",
                     help="only loop K1 launches (for counter collection), no JSON")
+    ap.add_argument("--select-only", action="store_true",
+                    help="only loop selector calls (for counter collection), no JSON")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="with --k1-only: also run device-to-device copies of this many MiB, the "
                          "calibration for the HBM byte counters")
@@ -497,6 +603,13 @@ def main():
     import synth
     device = "cuda:0"
     torch.cuda.set_device(0)
+
+    if args.select_only:
+        w = Workload(args.workload, device)
+        # (no time-based warm-up here: under a counter collection every launch is slow)
+        ms = time_loop(w.step, args.steps, args.warmup, warm_seconds=0.0)
+        log(f"[bench] select-only {args.workload}: {ms * 1e3:.2f} us/step")
+        return
 
     if args.k1_only:
         w = Workload(args.workload, device)
@@ -527,6 +640,7 @@ def main():
     main_w = main_res.pop("_workload")
     s = main_w.s
     extras = {"walk_modes": measure_modes(main_w, args.steps, args.warmup),
+              "gate": measure_gate(main_w, args.steps, args.warmup),
               "dynconv": measure_dynconv(device, args.steps, args.warmup),
               "lmhead_topk": measure_lmhead(device, args.steps, args.warmup)}
     log(f"[bench] extras: {extras}")
