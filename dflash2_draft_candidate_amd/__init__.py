@@ -246,6 +246,9 @@ def topk_lse(logits: torch.Tensor, k: int):
     return ids, unary, lse
 
 
+LMHEAD_MAX_ROWS = 16  # DFLASH2_LMHEAD_MAX_ROWS
+
+
 def lmhead_topk(hidden: torch.Tensor, W_lm: torch.Tensor, k: int):
     """hidden [R, H] bf16, W_lm [V, H] bf16 -> (cand_ids [R,k] int32, unary [R,k] f32, lse [R]
     f32) of the top-k pass over hidden . W_lm^T, computed without materialising the logits."""
@@ -258,9 +261,12 @@ def lmhead_topk(hidden: torch.Tensor, W_lm: torch.Tensor, k: int):
     ids = torch.empty((R, k), dtype=torch.int32, device=dev)
     unary = torch.empty((R, k), dtype=torch.float32, device=dev)
     lse = torch.empty((R,), dtype=torch.float32, device=dev)
+    if R > LMHEAD_MAX_ROWS:
+        raise Dflash2Error(-2, f"dflash2_lmhead_topk: R = {R} rows (at most {LMHEAD_MAX_ROWS}: "
+                               "use a product and topk_lse)")
     need = _lib.dflash2_lmhead_topk_workspace_bytes(R, H, V, k)
     if need == 0:
-        raise Dflash2Error(-1, "dflash2_lmhead_topk: unsupported sizes")
+        raise Dflash2Error(-1, "dflash2_lmhead_topk: invalid sizes")
     ws = _workspace(need, dev)
     rc = _lib.dflash2_lmhead_topk(_ptr(hidden), _ptr(W_lm), R, H, V, k, _ptr(ids), _ptr(unary),
                                   _ptr(lse), _ptr(ws), ws.numel(), _stream(dev))

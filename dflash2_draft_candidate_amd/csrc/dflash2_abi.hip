@@ -224,18 +224,22 @@ int dflash2_dynconv(const void *x, const void *base, const void *dyn, int dtype,
                                      static_cast<hipStream_t>(stream)));
 }
 
+static bool lmhead_args_valid(int R, int H, int V, int k) {
+    return R >= 1 && H >= 8 && H % 8 == 0 && V >= 1 && V <= DFLASH2_MAX_V && k >= 1 &&
+           k <= DFLASH2_LMHEAD_MAX_K && k <= lmhead_max_k() && k <= V;
+}
+
 size_t dflash2_lmhead_topk_workspace_bytes(int R, int H, int V, int k) {
-    if (R < 1 || H < 8 || H % 8 != 0 || V < 1 || V > DFLASH2_MAX_V || k < 1 ||
-        k > DFLASH2_LMHEAD_MAX_K || k > lmhead_max_k() || k > V)
-        return 0;
+    if (!lmhead_args_valid(R, H, V, k) || R > DFLASH2_LMHEAD_MAX_ROWS) return 0;
     return lmhead_workspace_bytes(R, V);
 }
 
 int dflash2_lmhead_topk(const void *hidden, const void *W_lm, int R, int H, int V, int k,
                         int32_t *cand_ids, float *unary, float *lse, void *workspace,
                         size_t workspace_bytes, void *stream) {
+    if (!lmhead_args_valid(R, H, V, k)) return DFLASH2_ERR_INVALID_ARG;
+    if (R > DFLASH2_LMHEAD_MAX_ROWS) return DFLASH2_ERR_UNSUPPORTED;
     const size_t need = dflash2_lmhead_topk_workspace_bytes(R, H, V, k);
-    if (need == 0) return DFLASH2_ERR_INVALID_ARG;
     int rc = check_ptrs({hidden, W_lm, cand_ids, unary});
     if (rc) return rc;
     if (lse && !aligned16(lse)) return DFLASH2_ERR_ALIGNMENT;

@@ -11,9 +11,10 @@
 // is one of the draft cycle's costs). Folding the top-k into the projection is this library's
 // design: it removes the [R, V] logits round trip through HBM.
 //
-// Design (gfx950, wave64; four waves per workgroup, no LDS staging of operands; RT = 1 row tile
-// of 16 for R <= 16, 2 for R <= 64, else 4):
-//   * Work. A workgroup takes a block of 16 * RT rows and a contiguous range of the vocabulary;
+// Design (gfx950, wave64; four waves per workgroup, no LDS staging of operands; one row tile of
+// 16 rows, R <= 16: the decode shape, where W_lm is read once and the pass is bound by that read;
+// with more row tiles the weight is reused and a library product with staged tiles is faster):
+//   * Work. A workgroup takes the (up to) 16 rows and a contiguous range of the vocabulary;
 //     its four waves split the range into contiguous runs of 16-column tiles, and a wave handles
 //     its run in passes over H of equal size (at most four tiles). Workgroups number their row blocks XCD by XCD, so the row
 //     blocks that read one vocabulary range share its W_lm lines in one L2.
@@ -47,6 +48,7 @@ constexpr int kLmWaves = 4;
 constexpr int kLmThreads = kLmWaves * kWave;
 constexpr int kLmGroup = 4;            // 16-column tiles per pass of a wave
 constexpr int kLmList = 16;            // keys kept per row (>= k)
+constexpr int kLmRowTiles = 1;         // 16-row tiles per workgroup (R <= 16)
 constexpr int kLmTargetWgs = 512;      // workgroups per launch (about two per CU)
 constexpr int kXcds = 8;
 constexpr int kDppRowShr1 = 0x111;     // row_shr:1 (within rows of 16 lanes)
@@ -211,7 +213,7 @@ struct LmJob {
     const uint16_t *hidden;  // [R, H]
     const uint16_t *W;       // [V, H]
     int R, H, V;
-    int rblocks;             // row blocks of 16 * RT rows
+    int rblocks;             // row blocks of 16 * RT rows (one)
     int ranges;              // vocabulary ranges (workgroups per row block)
     int col16;               // 16-column tiles in V
     uint64_t *part_keys;     // [R][ranges][kLmList]
@@ -219,9 +221,9 @@ struct LmJob {
 };
 
 // Workgroup (row block, range): the row block of one range on one XCD (see the header).
-template <int RT>
 __global__ __launch_bounds__(kLmThreads) void lmhead_topk_kernel(LmJob job) {
-    constexpr int D = RT == 4 ? 1 : (RT == 1 ? 4 : 2);  // steps of loads in flight (registers)
+    constexpr int RT = kLmRowTiles;
+    constexpr int D = 4;  // steps of loads in flight
     __shared__ uint64_t lists[kLmWaves][16 * RT][16];
     __shared__ float2 pairs[kLmWaves][16 * RT];
 
@@ -515,25 +517,18 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void lmhead_merge_kernel(
 }
 
 struct LmPlan {
-    int RT, rblocks, ranges, col16;
+    int rblocks, ranges, col16;
 };
 
 LmPlan plan_lmhead(int R, int V) {
     LmPlan p;
-    p.RT = R <= 16 ? 1 : (R <= 64 ? 2 : 4);
-    p.rblocks = (R + 16 * p.RT - 1) / (16 * p.RT);
+    p.rblocks = (R + 16 * kLmRowTiles - 1) / (16 * kLmRowTiles);
     p.col16 = (V + 15) / 16;
     int ranges = kLmTargetWgs / p.rblocks;
     if (ranges < 1) ranges = 1;
     const int most = (p.col16 + kLmWaves - 1) / kLmWaves;  // every wave gets a tile
     p.ranges = ranges < most ? ranges : most;
     return p;
-}
-
-template <int RT>
-void launch_rt(const LmJob &job, hipStream_t stream) {
-    hipLaunchKernelGGL((lmhead_topk_kernel<RT>), dim3((unsigned)(job.rblocks * job.ranges)),
-                       dim3(kLmThreads), 0, stream, job);
 }
 
 }  // namespace
@@ -560,12 +555,9 @@ hipError_t launch_lmhead_topk(const void *hidden, const void *W_lm, int R, int H
     job.col16 = p.col16;
     job.part_keys = static_cast<uint64_t *>(workspace);
     job.part_lse = reinterpret_cast<float2 *>(job.part_keys + (size_t)R * p.ranges * kLmList);
-    if (p.RT == 1)
-        launch_rt<1>(job, stream);
-    else if (p.RT == 2)
-        launch_rt<2>(job, stream);
-    else
-        launch_rt<4>(job, stream);
+    if (R > 16 * kLmRowTiles) return hipErrorInvalidValue;  // the C ABI refuses these sizes
+    hipLaunchKernelGGL(lmhead_topk_kernel, dim3((unsigned)(job.rblocks * job.ranges)),
+                       dim3(kLmThreads), 0, stream, job);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lmhead_merge_kernel, dim3((unsigned)R), dim3(kMergeWaves * kWave), 0, stream,

@@ -49,6 +49,7 @@ extern "C" {
 #define DFLASH2_MAX_V (1 << 28) /* largest vocabulary (a row's bytes stay within 32-bit offsets) */
 #define DFLASH2_MAX_CONV_TAPS 8 /* largest kernel of dflash2_dynconv */
 #define DFLASH2_LMHEAD_MAX_K 16 /* largest k of dflash2_lmhead_topk */
+#define DFLASH2_LMHEAD_MAX_ROWS 16 /* largest R of dflash2_lmhead_topk (one 16-row tile) */
 
 typedef enum dflash2_dtype {
     DFLASH2_F32 = 0,  /* IEEE binary32 */
@@ -256,8 +257,13 @@ int dflash2_dynconv(const void *x, const void *base, const void *dyn, int dtype,
  *   unary    [R, k]  fp32, device, out. x[i][cand_j] - lse_i.
  *   lse      [R]     fp32, device, out, may be NULL. logsumexp_v x[i][v].
  *   R >= 1; H >= 8 and H % 8 == 0; 1 <= V <= DFLASH2_MAX_V; 1 <= k <= min(V, DFLASH2_LMHEAD_MAX_K).
+ *   R <= DFLASH2_LMHEAD_MAX_ROWS (decode: one 16-row tile, where the weight is read once and the
+ *   pass is bound by that read); larger R returns DFLASH2_ERR_UNSUPPORTED: the pass stages no
+ *   operand tiles in LDS, so once several row tiles reuse the weight a library product followed
+ *   by dflash2_topk_lse is faster.
  * Workspace: dflash2_lmhead_topk_workspace_bytes(R, H, V, k) bytes (range partials), 16-byte
- * aligned, owned by the caller; contents need not be initialised. Errors: DFLASH2_ERR_INVALID_ARG,
+ * aligned, owned by the caller; contents need not be initialised (0 for sizes the pass refuses).
+ * Errors: DFLASH2_ERR_INVALID_ARG, DFLASH2_ERR_UNSUPPORTED (R > DFLASH2_LMHEAD_MAX_ROWS),
  * DFLASH2_ERR_ALIGNMENT (every pointer 16-byte aligned), DFLASH2_ERR_WORKSPACE, DFLASH2_ERR_HIP.
  */
 size_t dflash2_lmhead_topk_workspace_bytes(int R, int H, int V, int k);

@@ -176,6 +176,8 @@ def test_dynconv_rejects(lib, kw, status):
     (dict(H=0), EINVAL), (dict(R=0), EINVAL), (dict(V=0), EINVAL), (dict(hidden=None), EINVAL),
     (dict(W=None), EINVAL), (dict(ids=None), EINVAL), (dict(W=MIS), EALIGN),
     (dict(lse=MIS), EALIGN), (dict(ws=None), EWS), (dict(wsb=16), EWS), (dict(ws=MIS), EALIGN),
+    # more than one 16-row tile: refused (a library product and the top-k pass are faster there)
+    (dict(R=17), EUNSUP), (dict(R=1024), EUNSUP), (dict(R=17, k=0), EINVAL),
 ])
 def test_lmhead_rejects(lib, kw, status):
     a = dict(hidden=P, W=P, R=16, H=64, V=100, k=16, ids=P, un=P, lse=None, ws=P, wsb=1 << 30)
@@ -188,6 +190,7 @@ def test_lmhead_workspace_sizes(lib):
     assert lib.dflash2_lmhead_topk_workspace_bytes(16, 4096, 151936, 16) > 0
     assert lib.dflash2_lmhead_topk_workspace_bytes(16, 4096, 151936, 17) == 0
     assert lib.dflash2_lmhead_topk_workspace_bytes(16, 4100, 151936, 16) == 0
+    assert lib.dflash2_lmhead_topk_workspace_bytes(17, 4096, 151936, 16) == 0
 
 
 def test_binding_rejects_host_tensors():

@@ -102,7 +102,7 @@ def _stage_cases(seed: int) -> dict:
                           G * int(pick([1, 2, 3, 8, 64, 256])), int(pick([1, 2, 3, 4, 8])), G,
                           pick(["f32", "bf16"])))
         V = int(pick([16, 17, 100, 1000, 4099, 20011]))
-        c["lm"].append((int(pick([1, 5, 16, 33, 64, 70, 130])), int(pick([8, 64, 96, 200, 1024])),
+        c["lm"].append((int(pick([1, 5, 16, 3, 9, 13, 11])), int(pick([8, 64, 96, 200, 1024])),
                         V, int(min(V, pick([1, 4, 8, 15, 16]))), int(rng.integers(0, 1000))))
     for _ in range(8):
         c["walk_ex"].append((int(rng.integers(1, 9)), int(rng.integers(1, 41)),
