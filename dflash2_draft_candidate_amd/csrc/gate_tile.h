@@ -19,8 +19,6 @@
 
 namespace dflash2 {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Waves sharing one tile's range of H. (Eight waves at 8 column tiles, each with half the
 // steps, took as long: the tile costs the stream the same wave-time either way.)

@@ -41,8 +41,6 @@
 namespace dflash2 {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kLmWaves = 4;
 constexpr int kLmThreads = kLmWaves * kWave;

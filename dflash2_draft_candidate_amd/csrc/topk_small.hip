@@ -32,6 +32,7 @@
 //   * gate (optional): workgroups past the slices compute split-K tiles of hidden . W_sel with
 //     the stand-alone gate kernel's decomposition and summation order (gate_tile.h; its first
 //     four waves), so a fused selector call reproduces the stage-by-stage gate bit for bit.
+#include "arrival.h"
 #include "device_common.h"
 #include "gate_tile.h"
 #include "kernels.h"
@@ -247,9 +248,7 @@ __global__ __launch_bounds__(kSmThreads) void topk_small_kernel(
     // Launch epochs grow, so an atomic max of (epoch, 0) re-bases a counter left by an earlier
     // launch and leaves one of this launch alone; it is not waited for.
     const int64_t row = unit / S;
-    if (S > 1 && threadIdx.x == 0)
-        __hip_atomic_fetch_max(&arrivals[row], (uint64_t)epoch << 32, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+    if (S > 1 && threadIdx.x == 0) arrival_rebase(&arrivals[row], epoch);
     te.xh = te.xt = -INFINITY;
     const bool ragged = wave == 0 && (ur.h1 > ur.h0 || ur.t1 > ur.t0);
     if (ragged) {  // the ragged ends hold fewer than 2 * EV elements
@@ -382,37 +381,8 @@ __global__ __launch_bounds__(kSmThreads) void topk_small_kernel(
                 __hip_atomic_store(reinterpret_cast<uint64_t *>(&part_lse[unit]),
                                    ((uint64_t)__float_as_uint(s0) << 32) | __float_as_uint(r0),
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            // (the signal fences keep the compiler from moving the stores or the count across
-            // the wait; they emit nothing)
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0), expcnt(0), lgkmcnt(0)
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            if (lane == 0) {
-                // The counter carries this launch's epoch above the count: an arrival adds one,
-                // and the one that makes the count S is the last. An arrival that still finds
-                // another launch's epoch (a counter holding a larger one, never set or wrapped)
-                // re-bases it to (epoch, 0) unless another arrival has, then adds again: the adds
-                // made to stale values are dropped with them, and every arrival that made one
-                // repeats it.
-                uint64_t *ctr = &arrivals[row];
-                uint64_t old = __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT);
-                if ((uint32_t)(old >> 32) != epoch) {
-                    uint64_t cur = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    while ((uint32_t)(cur >> 32) != epoch) {
-                        __hip_atomic_compare_exchange_strong(ctr, &cur, (uint64_t)epoch << 32,
-                                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                             __HIP_MEMORY_SCOPE_AGENT);
-                        // success or failure, cur now holds a value of this launch or a stale
-                        // one changed by another arrival
-                        if ((uint32_t)(cur >> 32) != epoch)
-                            cur = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    }
-                    old = __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-                }
-                sh.last = (uint32_t)old + 1u == (uint32_t)S ? 1u : 0u;
-            }
+            stores_complete();
+            if (lane == 0) sh.last = arrive(&arrivals[row], epoch, (uint32_t)S) ? 1u : 0u;
         }
     }
     if (S == 1) return;
@@ -461,8 +431,7 @@ __global__ __launch_bounds__(kSmThreads) void topk_small_kernel(
         if (lse_out) lse_out[row] = (float)lse;
         // every slice of this launch has counted itself: clear the count for a replay of the
         // same launch (same epoch)
-        __hip_atomic_store(&arrivals[row], (uint64_t)epoch << 32, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        arrival_clear(&arrivals[row], epoch);
     }
 }
 
