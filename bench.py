@@ -10,8 +10,10 @@ its logits from HBM. The weights (W_sel, codebooks) are one copy, as in serving.
 Prints one JSON line:
   value        selector positions/s = B*L*steps / elapsed (the default workload: serving-b64)
   roofline     K1 (the top-k/logsumexp pass, the dominant kernel): algorithmic bytes per launch
-               (R*V*elem + R*k*8 + R*4) / mean K1 launch time (HIP events around a loop of K1-only
-               launches on the launch stream), against the MI355X HBM peak of 8 TB/s; `traffic`
+               (R*V*elem + R*k*8 + R*4) / mean K1 launch time (HIP events around graph replays of
+               K1-only launches on the launch stream; the eager loop's time, which also holds the
+               dispatch gap between launches, is given beside it), against the MI355X HBM peak of
+               8 TB/s; `traffic`
                comes from committed rocprofv3 counter readings when they match the current kernel
   cpu_baseline the fp64 C oracle on the host, on the same workload: row-parallel over the host's
                cores (value, cores) and single-threaded (single_thread), with the CPU model
@@ -203,6 +205,7 @@ def measure(name: str, device: str, steps: int, warmup: int) -> dict:
     replays = max(1, steps // n_graph)
     e2e_graph_ms = graph_loop(w.step, n_graph, replays)
     k1_graph_ms = graph_loop(lambda i: w.k1_step(i, ids, unary, lse, ws), n_graph, replays)
+    gbs_graph = k1_bytes(s) / (k1_graph_ms * 1e-3) / 1e9
     res = {"B": s.B, "L": s.L, "k": s.k, "V": s.V, "H": s.H, "r": s.r,
            "logits": s.logits_dtype, "e2e_us": round(e2e_ms * 1e3, 2),
            "positions_per_s": round(s.R / (e2e_ms * 1e-3), 1), "k1_us": round(k1_ms * 1e3, 2),
@@ -210,7 +213,9 @@ def measure(name: str, device: str, steps: int, warmup: int) -> dict:
            "e2e_us_per_step": e2e_stats, "k1_us_per_step": k1_stats,
            "graph": {"calls_per_graph": n_graph, "replays": replays,
                      "e2e_us": round(e2e_graph_ms * 1e3, 2),
-                     "k1_us": round(k1_graph_ms * 1e3, 2)}}
+                     "positions_per_s": round(s.R / (e2e_graph_ms * 1e-3), 1),
+                     "k1_us": round(k1_graph_ms * 1e3, 2), "k1_gbs": round(gbs_graph, 1),
+                     "k1_frac": round(gbs_graph / PEAK_HBM_GBS, 4)}}
     res["_workload"] = w
     return res
 
@@ -658,12 +663,16 @@ def main():
             log(f"[bench] {name}: {r}")
 
     traffic = committed_traffic()
-    roof = {"bound": "hbm", "achieved": main_res["k1_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": main_res["k1_frac"],
+    # the kernel's launch time: HIP events around graph replays of K1 launches (the eager loop's
+    # per-launch time also holds the dispatch gap between launches; both are in per_config)
+    g = main_res["graph"]
+    roof = {"bound": "hbm", "achieved": g["k1_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": g["k1_frac"],
             "traffic": traffic["bytes_per_launch"] if traffic and
             traffic.get("workload") == args.workload else None,
             "kernel": "topk_lse_kernel", "algorithmic_bytes_per_launch": k1_bytes(s),
-            "launch_us": main_res["k1_us"]}
+            "launch_us": g["k1_us"], "timing": "graph replay of K1 launches, HIP events",
+            "eager_launch_us": main_res["k1_us"]}
     line = {
         "metric": METRIC,
         "value": main_res["positions_per_s"],
