@@ -112,7 +112,8 @@ struct K1Shared {
     uint32_t q_tail[kMaxUnits];       // queue slots reserved so far
     uint32_t q_head[kMaxUnits];       // queue slots consumed by the owner so far
     uint32_t spilled;                 // bit s: slot s kept candidates in its own list
-    uint64_t lists[kWaves * kWave];   // spilled lists, for the final merge
+    uint64_t lists[kWaves * kWave];   // during the stream: each wave's staged vectors;
+                                      // after it: spilled lists, for the final merge
     uint32_t seed_vals[kWaves * kWave];  // seed maxima; after the stream: partial chunk sums
     float rag[kMaxUnits * kWave];     // the unit's ragged-end sums per lane
     u32x4 stage[kWaves][kU];          // per wave: one hit lane's batch, read back transposed
@@ -421,17 +422,59 @@ __device__ __forceinline__ void unpack_batch(const u32x4 *buf, int nvalid, int l
     for (int j = 1; j < kU * EV; ++j) bmax = fmaxf(bmax, x[j]);
 }
 
+// Candidates of one element position set: the lanes in m hold one each, with key `key`. The
+// owner inserts them into its list one by one; another wave queues them to the owner in
+// consecutive slots reserved at once (if the queue is full, a wave of the unit keeps them in a
+// list of its own, merged at the end, and a wave helping another unit waits for room).
+__device__ __forceinline__ void emit_keys(WaveTopk &w, uint64_t m, uint64_t key, int lane) {
+    if (!w.owner) {
+        const uint32_t n = (uint32_t)__popcll(m);
+        for (;;) {
+            uint32_t pos;
+            if (try_reserve(w, lane, n, pos)) {
+                if ((m >> lane) & 1ull) {
+                    const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
+                        (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    __hip_atomic_store(&w.queue[(pos + rank) & w.qmask], key, __ATOMIC_RELEASE,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+                }
+                return;
+            }
+            if (w.home) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        w.spilled = true;  // the queue was full: this wave keeps them
+    }
+    while (m != 0ull) {
+        const int src = __builtin_ctzll(m);
+        m &= m - 1ull;
+        const uint64_t c = lane_value(key, src);
+        if (c > w.tau_key) wave_insert(w, c, lane);
+    }
+}
+
+// Vectors staged at once by a batch's candidate pass (as floats: kStageVecs * kVecElems of them
+// per wave in its part of the spilled lists' area, which those use only after the stream).
+constexpr int kStageVecs = 16;
+constexpr int kVecElems = 8;  // floats per staged vector (a 16-byte vector of bf16)
+
 // One batch: add its terms 2^(x log2e - R) to the lane's chunk sum and offer it to the list.
-// A lane's batch sum is at least its largest term, so a lane whose sum is below the threshold's
-// term (t_e = 2^(tau log2e - R), less a margin for exp2's rounding) holds no candidate, and no
-// lane maximum is needed. When t_e underflows to 0, or the sums flag more than kMaxSumHits lanes
-// (near-flat rows, where every sum is large), the lane maxima decide instead.
+// Each lane sums its kU vectors separately and adds the four sums in a fixed order. A vector's
+// sum is at least its largest term, so a vector whose sum is below the threshold's term
+// (t_e = 2^(tau log2e - R), less a margin for exp2's rounding) holds no candidate, and no
+// maximum is needed. When t_e underflows to 0, or the sums flag more than kMaxSumHits lanes
+// (near-flat rows, where every sum is large), each vector's maximum decides instead. The
+// flagged vectors (as floats) are staged in the wave's LDS area kStageVecs at a time, in rank
+// order, and read back transposed (lane i <- staged element i), so one staging round trip
+// serves the whole batch; each element at or above the threshold is handed on (emit_keys).
 template <typename T, bool PARTIAL>
 __device__ __forceinline__ void batch(const u32x4 *buf, int nvalid, int32_t id_base, float R,
                                       float t_e, float &csum, WaveTopk &w, int lane,
-                                      u32x4 *stage) {
+                                      float *vstage, int32_t *vid) {
     constexpr int EV = Elem<T>::kPerVec;
     constexpr int NB = kU * EV;
+    static_assert(kU == 4, "the vector sums are added as (s0 + s1) + (s2 + s3)");
+    static_assert(EV <= kVecElems, "a staged vector holds a 16-byte vector's elements");
     float x[NB];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -441,19 +484,68 @@ __device__ __forceinline__ void batch(const u32x4 *buf, int nvalid, int32_t id_b
             for (int e = 0; e < EV; ++e) x[u * EV + e] = -INFINITY;
         }
     }
-    float bs = __builtin_amdgcn_exp2f(fmaf(x[0], kLog2e, -R));
+    float vs[kU];
 #pragma unroll
-    for (int j = 1; j < NB; ++j) bs += __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -R));
-    csum += bs;
-    uint64_t hits = __ballot(bs >= t_e);
-    if (t_e == 0.f || __popcll(hits) > kMaxSumHits) {
-        // the sums do not single out a few lanes (e.g. near-flat rows): use the lane maxima
-        float bmax = x[0];
+    for (int u = 0; u < kU; ++u) {
+        vs[u] = __builtin_amdgcn_exp2f(fmaf(x[u * EV], kLog2e, -R));
 #pragma unroll
-        for (int j = 1; j < NB; ++j) bmax = fmaxf(bmax, x[j]);
-        hits = __ballot(bmax != -INFINITY && bmax >= w.tau_v);
+        for (int e = 1; e < EV; ++e) vs[u] += __builtin_amdgcn_exp2f(fmaf(x[u * EV + e], kLog2e, -R));
     }
-    offer_lanes<T, kU, (NB < kWave ? NB : kWave)>(w, buf, hits, nvalid, id_base, EV, lane, stage);
+    const float bs = (vs[0] + vs[1]) + (vs[2] + vs[3]);
+    csum += bs;
+    // (the lane sum is at least each vector sum, so the lanes test first)
+    const uint64_t any = __ballot(bs >= t_e);
+    if (any == 0ull && t_e != 0.f) return;
+    // bit u: vector u may hold a candidate
+    uint32_t fl = (vs[0] >= t_e ? 1u : 0u) | (vs[1] >= t_e ? 2u : 0u) |
+                  (vs[2] >= t_e ? 4u : 0u) | (vs[3] >= t_e ? 8u : 0u);
+    if (t_e == 0.f || __popcll(any) > kMaxSumHits) {
+        // the sums do not single out a few lanes (e.g. near-flat rows): the vectors' maxima
+        fl = 0u;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            float vm = x[u * EV];
+#pragma unroll
+            for (int e = 1; e < EV; ++e) vm = fmaxf(vm, x[u * EV + e]);
+            fl |= (vm != -INFINITY && vm >= w.tau_v) ? (1u << u) : 0u;
+        }
+    }
+    uint32_t P = 0u;  // flagged vectors
+#pragma unroll
+    for (int u = 0; u < kU; ++u) P += (uint32_t)__popcll(__ballot((fl >> u) & 1u));
+    for (uint32_t r0 = 0u; r0 < P; r0 += kStageVecs) {
+        // rank of a flagged vector: those of lower u first, then by lane; ranks r0 ... go now
+        uint32_t below = 0u;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const uint64_t hu = __ballot((fl >> u) & 1u);
+            const uint32_t r = below - r0 + __builtin_amdgcn_mbcnt_hi(
+                                                (uint32_t)(hu >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)hu, 0u));
+            if (((fl >> u) & 1u) && r < (uint32_t)kStageVecs) {  // (r wraps below r0)
+#pragma unroll
+                for (int e = 0; e < EV; e += 4)
+                    *reinterpret_cast<f32x4 *>(vstage + r * kVecElems + e) =
+                        f32x4{x[u * EV + e], x[u * EV + e + 1], x[u * EV + e + 2],
+                              x[u * EV + e + 3]};
+                vid[r] = id_base + (u * kWave + lane) * EV;
+            }
+            below += (uint32_t)__popcll(hu);
+        }
+        const uint32_t nv_st = min(P - r0, (uint32_t)kStageVecs);
+        for (uint32_t base = 0u; base < nv_st * kVecElems; base += kWave) {
+            const uint32_t i = base + (uint32_t)lane;
+            const uint32_t v = i / kVecElems, e = i % kVecElems;
+            float xi = -INFINITY;
+            int32_t id = 0;
+            if (v < nv_st && e < (uint32_t)EV) {
+                xi = vstage[i];
+                id = vid[v] + (int32_t)e;
+            }
+            const uint64_t m = __ballot(xi >= w.tau_v && xi != -INFINITY);
+            if (m != 0ull) emit_keys(w, m, cand_key(xi, id), lane);
+        }
+    }
 }
 
 // Unit q and index wv within the unit of wave slot s, mixing the SIMD age classes (slot s sits
@@ -529,6 +621,10 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     const int P = (kRing + CB - 1) / CB;      // chunks per wave assigned up front
     float *csums = chunk_sums + (size_t)q * nch_max * kWave;
     u32x4 *stage = sh.stage[wave];
+    // flagged vectors staged by a batch (floats) and their first ids: the wave's part of the
+    // spilled lists' area (used by those only after the stream) and its stage
+    float *vstage = reinterpret_cast<float *>(sh.lists + wave * kWave);
+    int32_t *vid = reinterpret_cast<int32_t *>(sh.stage[wave]);
 
     if (threadIdx.x < kMaxUnits) {
         sh.tau[threadIdx.x] = 0ull;
@@ -834,9 +930,9 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
             const int nvalid = min(kStep, p_nv - b * kStep);
             const int32_t id_base = idb0 + b * kStep * EV;
             if (nvalid < kStep)
-                batch<T, true>(ring[j], nvalid, id_base, R, t_e, csum, w, lane, stage);
+                batch<T, true>(ring[j], nvalid, id_base, R, t_e, csum, w, lane, vstage, vid);
             else
-                batch<T, false>(ring[j], kStep, id_base, R, t_e, csum, w, lane, stage);
+                batch<T, false>(ring[j], kStep, id_base, R, t_e, csum, w, lane, vstage, vid);
             if (s_flags[j] & 4) {
                 chunk_sums[((size_t)pq * nch_max + s_c[j]) * kWave + lane] = csum;
                 if (__ballot(!(csum <= kSumLimit)) != 0ull && lane == 0) sh.overflow[pq] = 1u;
