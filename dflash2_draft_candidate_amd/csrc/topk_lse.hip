@@ -26,23 +26,25 @@
 //   * top-k. A 64-bit key (order-preserving logit map above the inverted id) makes the candidate
 //     order one unsigned compare. The unit's oldest wave (its owner) keeps the unit's 64 best
 //     keys sorted across its lanes; the other waves queue their candidates to it through LDS,
-//     the survivors of one staged lane in consecutive slots reserved with one atomic (a wave
-//     that finds the queue full keeps them in a list of its own, merged at the end). An
-//     element is admitted only if it beats the unit's threshold in LDS, which is always valid
-//     (k real elements at or above it): the k-th key of a wave's list, or the seed below. A
-//     batch costs one compare per lane of the lane's term sum unless it reaches the threshold's
-//     term; then each such lane's batch is staged in LDS and read back transposed (lane j <-
-//     element j), and the owner inserts each surviving candidate by ballot + popcount rank and
-//     a one-lane DPP shift. After its stream the owner takes what is queued 64 at a time and,
-//     when more than a few pass the threshold, sorts them and merges the two sorted lists.
+//     each element set in consecutive slots reserved with one atomic add (a wave waits for
+//     room if the owner is a lap behind; the owner always catches up). An element is admitted
+//     only if it beats the unit's threshold in LDS, which is always valid (k real elements at
+//     or above it): the k-th key of the owner's list, or the seed below. A batch costs one
+//     compare per lane of the lane's term sum unless it reaches the threshold's term; then the
+//     batch's flagged vectors (by their own sums, or their maxima in near-flat rows) are staged
+//     in LDS together and read back transposed (lane i <- staged element i), and the owner
+//     inserts each surviving candidate by ballot + popcount rank and a one-lane DPP shift.
+//     After its stream the owner takes what is queued 64 at a time and, when more than a few
+//     pass the threshold, sorts them and merges the two sorted lists.
 //   * Seed. The threshold starts at the k-th largest of the lane maxima of the unit's waves over
 //     their first batches (k real elements reach it); with more than four waves per unit, the
 //     k-th largest of the lane-wise maxima over the waves (one search instead of one per
 //     wave, so small units get it before most of their batches are read).
 //   * End. The owner keeps draining the queue until every wave of its unit has finished the
 //     stream; after a barrier each wave adds a fixed range of the unit's chunk sums, and the
-//     owner merges any kept lists (bitonic merge: the top k of distinct keys is unique), adds the
-//     partial sums in wave order and writes the results. Deterministic throughout.
+//     owner takes what is left in the queue, adds the partial sums in wave order and writes the
+//     results (the top k of distinct keys is unique, whatever the order they arrived in).
+//     Deterministic throughout.
 //   * Fused gate (bf16 activations, r <= 128). The selector's gate product is independent of
 //     the logits, so the top-k pass can carry it: workgroup t computes split-K tile t of
 //     hidden . W_sel (the same tiles, wave ranges and summation order as the stand-alone gate
@@ -111,9 +113,7 @@ struct K1Shared {
                                       // unit q owns slots [q, q + 1) * kQueueSlots / G
     uint32_t q_tail[kMaxUnits];       // queue slots reserved so far
     uint32_t q_head[kMaxUnits];       // queue slots consumed by the owner so far
-    uint32_t spilled;                 // bit s: slot s kept candidates in its own list
-    uint64_t lists[kWaves * kWave];   // during the stream: each wave's staged vectors;
-                                      // after it: spilled lists, for the final merge
+    alignas(16) float vstage[kWaves][128];  // each wave's flagged vectors staged by a batch
     uint32_t seed_vals[kWaves * kWave];  // seed maxima; after the stream: partial chunk sums
     float rag[kMaxUnits * kWave];     // the unit's ragged-end sums per lane
     u32x4 stage[kWaves][kU];          // per wave: one hit lane's batch, read back transposed
@@ -207,7 +207,6 @@ struct WaveTopk {
     uint32_t head;         // owner: slots consumed
     bool owner;            // this wave keeps the unit's list
     bool home;             // the unit being processed is the wave's own (else it helps another)
-    bool spilled;          // a non-owner that had to keep candidates itself
 };
 
 // Key 0 (no threshold yet) admits every element: its logit is -inf, not the NaN the key map
@@ -244,28 +243,6 @@ __device__ __forceinline__ void wave_insert(WaveTopk &w, uint64_t c, int lane) {
     raise_tau(w, lane_value(w.top, w.k - 1), lane);
 }
 
-// Reserve n consecutive queue slots if the queue has room for them (their previous occupants
-// consumed).
-__device__ __forceinline__ bool try_reserve(WaveTopk &w, int lane, uint32_t n, uint32_t &pos) {
-    uint32_t ok = 0u, p = 0u;
-    if (lane == 0) {
-        const uint32_t head =
-            __hip_atomic_load(w.q_head, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
-        uint32_t tail = __hip_atomic_load(w.q_tail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        while (tail + n - head <= w.qmask + 1u) {
-            if (__hip_atomic_compare_exchange_strong(w.q_tail, &tail, tail + n, __ATOMIC_RELAXED,
-                                                     __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_WORKGROUP)) {
-                ok = 1u;
-                p = tail;
-                break;
-            }
-        }
-    }
-    pos = __builtin_amdgcn_readfirstlane(p);
-    return __builtin_amdgcn_readfirstlane(ok) != 0u;
-}
-
 // Candidates above which a set is sorted and merged into the list in one go instead of being
 // inserted one at a time (a bitonic sort and merge cost about as much as this many inserts).
 constexpr int kBulkInsert = 6;
@@ -291,31 +268,43 @@ __device__ __forceinline__ void insert_set(WaveTopk &w, uint64_t c, int lane) {
     }
 }
 
-// A non-owner's candidates: lanes in m, lane j holding logit x with id `id0 + j_offset(j)`.
-// They go to the owner's queue in consecutive slots reserved at once (each lane builds its own
-// key only for the store); true once queued. If the queue has no room, a wave of the unit gets
-// false and keeps them in its own list (merged at the end), and a wave helping from another
-// unit waits for room (the owner drains until every wave is done). Reserved slots are written
-// at once, so the queue never holds a hole for long. Keys at or below the threshold may be
-// queued; the owner drops them.
-template <int EV>
-__device__ __forceinline__ bool queue_set(WaveTopk &w, uint64_t m, float x, int32_t id0,
-                                          int lane) {
-    const uint32_t n = (uint32_t)__popcll(m);
-    for (;;) {
-        uint32_t pos;
-        if (try_reserve(w, lane, n, pos)) {
-            if ((m >> lane) & 1ull) {
-                const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
-                    (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                const int32_t id = id0 + (lane / EV) * kWave * EV + (lane % EV);
-                __hip_atomic_store(&w.queue[(pos + rank) & w.qmask], cand_key(x, id),
-                                   __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-            }
-            return true;
+// Reserve n consecutive queue slots (one atomic add) and wait until the owner has consumed what
+// they held a lap before. The owner takes the queue in order and keeps doing so until every wave
+// of the workgroup is done, so the wait ends; a reserved slot is always written afterwards (the
+// owner stops at a slot not yet written).
+__device__ __forceinline__ uint32_t reserve_slots(WaveTopk &w, int lane, uint32_t n) {
+    uint32_t p = 0u;
+    if (lane == 0) {
+        p = __hip_atomic_fetch_add(w.q_tail, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        uint32_t head =
+            __hip_atomic_load(w.q_head, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        while (p + n - head > w.qmask + 1u) {
+            __builtin_amdgcn_s_sleep(1);
+            head = __hip_atomic_load(w.q_head, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
-        if (w.home) return false;
-        __builtin_amdgcn_s_sleep(1);
+    }
+    return __builtin_amdgcn_readfirstlane(p);
+}
+
+// Candidates of one element position set: the lanes in m hold one each, with key `key`. The
+// owner inserts them into its list one by one; another wave queues them to the owner in
+// consecutive slots reserved at once.
+__device__ __forceinline__ void emit_keys(WaveTopk &w, uint64_t m, uint64_t key, int lane) {
+    if (!w.owner) {
+        const uint32_t pos = reserve_slots(w, lane, (uint32_t)__popcll(m));
+        if ((m >> lane) & 1ull) {
+            const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
+                (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            __hip_atomic_store(&w.queue[(pos + rank) & w.qmask], key, __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        return;
+    }
+    while (m != 0ull) {
+        const int src = __builtin_ctzll(m);
+        m &= m - 1ull;
+        const uint64_t c = lane_value(key, src);
+        if (c > w.tau_key) wave_insert(w, c, lane);
     }
 }
 
@@ -375,21 +364,10 @@ __device__ __forceinline__ void offer_lanes(WaveTopk &w, const u32x4 *buf, uint6
         float x = -INFINITY;
         if (j < NSLOT) x = Elem<T>::lds_element(stage, j);
         const bool maybe = j < NSLOT && vec_j + L < nvalid && x >= w.tau_v && x != -INFINITY;
-        uint64_t m = __ballot(maybe);
-        if (m == 0ull) continue;
-        const int32_t id0 = id_base + L * lane_stride;
-        if (!w.owner) {
-            if (queue_set<EV>(w, m, x, id0, lane)) continue;
-            w.spilled = true;  // the queue was full: this wave keeps them
-        }
-        while (m != 0ull) {
-            // inserted one by one; each key is built from wave-uniform values
-            const int src = __builtin_ctzll(m);
-            m &= m - 1ull;
-            const float xs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), src));
-            const uint64_t c = cand_key(xs, id0 + (src / EV) * kWave * EV + (src % EV));
-            if (c > w.tau_key) wave_insert(w, c, lane);
-        }
+        const uint64_t m = __ballot(maybe);
+        if (m != 0ull)
+            emit_keys(w, m, cand_key(x, id_base + L * lane_stride + (j / EV) * kWave * EV + (j % EV)),
+                      lane);
     }
 }
 
@@ -422,41 +400,12 @@ __device__ __forceinline__ void unpack_batch(const u32x4 *buf, int nvalid, int l
     for (int j = 1; j < kU * EV; ++j) bmax = fmaxf(bmax, x[j]);
 }
 
-// Candidates of one element position set: the lanes in m hold one each, with key `key`. The
-// owner inserts them into its list one by one; another wave queues them to the owner in
-// consecutive slots reserved at once (if the queue is full, a wave of the unit keeps them in a
-// list of its own, merged at the end, and a wave helping another unit waits for room).
-__device__ __forceinline__ void emit_keys(WaveTopk &w, uint64_t m, uint64_t key, int lane) {
-    if (!w.owner) {
-        const uint32_t n = (uint32_t)__popcll(m);
-        for (;;) {
-            uint32_t pos;
-            if (try_reserve(w, lane, n, pos)) {
-                if ((m >> lane) & 1ull) {
-                    const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
-                        (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                    __hip_atomic_store(&w.queue[(pos + rank) & w.qmask], key, __ATOMIC_RELEASE,
-                                       __HIP_MEMORY_SCOPE_WORKGROUP);
-                }
-                return;
-            }
-            if (w.home) break;
-            __builtin_amdgcn_s_sleep(1);
-        }
-        w.spilled = true;  // the queue was full: this wave keeps them
-    }
-    while (m != 0ull) {
-        const int src = __builtin_ctzll(m);
-        m &= m - 1ull;
-        const uint64_t c = lane_value(key, src);
-        if (c > w.tau_key) wave_insert(w, c, lane);
-    }
-}
-
 // Vectors staged at once by a batch's candidate pass (as floats: kStageVecs * kVecElems of them
-// per wave in its part of the spilled lists' area, which those use only after the stream).
+// per wave, in its row of K1Shared::vstage).
 constexpr int kStageVecs = 16;
 constexpr int kVecElems = 8;  // floats per staged vector (a 16-byte vector of bf16)
+static_assert(kStageVecs * kVecElems == 128, "K1Shared::vstage holds one stage per wave");
+static_assert(kStageVecs * 4 <= kU * 16, "the staged vectors' ids fit the wave's stage");
 
 // One batch: add its terms 2^(x log2e - R) to the lane's chunk sum and offer it to the list.
 // Each lane sums its kU vectors separately and adds the four sums in a fixed order. A vector's
@@ -609,9 +558,6 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     constexpr int W = kWaves / G;
     int q, wv;
     wave_unit<G>(wave, q, wv);
-    uint32_t peers = 0u;  // slots of the unit's waves
-#pragma unroll
-    for (int i = 0; i < W; ++i) peers |= 1u << unit_slot<G>(q, i);
     const int64_t unit = (int64_t)blockIdx.x * G + q;
     const bool active = unit < n_units;  // trailing units of the last workgroup idle
     const UnitRange ur = unit_range(active ? unit : 0, V, S, EV);
@@ -621,9 +567,9 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     const int P = (kRing + CB - 1) / CB;      // chunks per wave assigned up front
     float *csums = chunk_sums + (size_t)q * nch_max * kWave;
     u32x4 *stage = sh.stage[wave];
-    // flagged vectors staged by a batch (floats) and their first ids: the wave's part of the
-    // spilled lists' area (used by those only after the stream) and its stage
-    float *vstage = reinterpret_cast<float *>(sh.lists + wave * kWave);
+    // flagged vectors staged by a batch (floats) and their first ids (in the wave's stage,
+    // which the ragged ends use only before the stream)
+    float *vstage = sh.vstage[wave];
     int32_t *vid = reinterpret_cast<int32_t *>(sh.stage[wave]);
 
     if (threadIdx.x < kMaxUnits) {
@@ -632,7 +578,6 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
         sh.overflow[threadIdx.x] = 0u;
     }
     if (threadIdx.x < kMaxUnits) sh.q_tail[threadIdx.x] = sh.q_head[threadIdx.x] = 0u;
-    if (threadIdx.x == 0) sh.spilled = 0u;
     for (int i = threadIdx.x; i < kQueueSlots; i += kThreads) sh.queue[i] = 0ull;
     if (threadIdx.x < kMaxUnits) sh.seeded[threadIdx.x] = sh.seed_done[threadIdx.x] = 0u;
     if (threadIdx.x == 0) sh.gate_arrived = sh.done_all = 0u;
@@ -779,7 +724,6 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     w.head = 0u;
     w.owner = active && wv == 0;  // the unit's oldest wave keeps its list
     w.home = true;
-    w.spilled = false;
     set_tau(w, 0ull);
     // Threshold seed: the wave starts from the k-th largest of its own 64 lane maxima, then
     // publishes them; the unit's last wave to publish raises the unit threshold to the k-th
@@ -954,10 +898,9 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
             __builtin_amdgcn_s_sleep(2);
         }
     }
-    // Every wave is done, so every reserved queue slot is final and every chunk sum is in LDS.
-    // Each wave of a unit adds a fixed range of its chunk sums (per lane, in chunk order); the
-    // owner takes what is left in the queue and merges the lists of any wave that had to keep
-    // candidates itself.
+    // Every wave is done, so every reserved queue slot is written and every chunk sum is in
+    // LDS. Each wave of a unit adds a fixed range of its chunk sums (per lane, in chunk order);
+    // the owner takes what is left in the queue.
     __syncthreads();
     float *psum = reinterpret_cast<float *>(sh.seed_vals);
     if (active) {
@@ -974,21 +917,9 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
         for (; c < c1; ++c) t += csums[c * kWave + lane];
         psum[wave * kWave + lane] = t;
     }
-    if (w.spilled) {
-        sh.lists[wave * kWave + lane] = w.top;
-        if (lane == 0)
-            __hip_atomic_fetch_or(&sh.spilled, 1u << wave, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
     __syncthreads();
     if (!rag_owner) return;
     drain<true>(w, lane, true);
-    uint32_t sp = sh.spilled & peers;
-    while (sp != 0u) {
-        const int s = __builtin_ctz(sp);
-        sp &= sp - 1u;
-        w.top = wave_merge_desc(w.top, sh.lists[s * kWave + lane], lane);
-    }
     // The unit's logsumexp: the waves' partial sums per lane in wave order, then the ragged
     // sums, then across lanes (fixed order); lse = (R + log2 total) ln 2.
     float ref = R, sum = 0.f;
