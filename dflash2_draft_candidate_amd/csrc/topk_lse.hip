@@ -76,7 +76,7 @@ constexpr size_t kLdsDynamicMax = 136 * 1024;  // chunk sums + a fused gate's ti
 constexpr float kSumLimit = 0x1p100f;     // a chunk sum above this leaves the fast path
 constexpr float kSumFloor = 0x1p-60f;     // so does a unit total below this
 constexpr float kTermMargin = 1.f - 0x1p-10f;  // v_exp_f32 is far more accurate than this
-constexpr int kMaxSumHits = 4;            // lanes the sum filter may flag before maxima decide
+constexpr int kMaxSumHits = 8;            // lanes the sum filter may flag before maxima decide
 constexpr int kQueueSlots = 512;          // candidate queue slots per workgroup (G units share)
 constexpr int kSeedBatches = 3;           // batches per wave behind the seed (<= kRing)
 constexpr int kBufferWord3 = 0x00020000;  // gfx9-family buffer descriptor word 3 (raw data)
