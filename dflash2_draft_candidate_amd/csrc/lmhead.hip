@@ -11,30 +11,36 @@
 // is one of the draft cycle's costs). Folding the top-k into the projection is this library's
 // design: it removes the [R, V] logits round trip through HBM.
 //
-// Design (gfx950, wave64; four waves per workgroup, no LDS staging of operands; one row tile of
-// 16 rows, R <= 16: the decode shape, where W_lm is read once and the pass is bound by that read;
-// with more row tiles the weight is reused and a library product with staged tiles is faster):
-//   * Work. A workgroup takes the (up to) 16 rows and a contiguous range of the vocabulary;
-//     its four waves split the range into contiguous runs of 16-column tiles, and a wave handles
-//     its run in passes over H of equal size (at most four tiles). Workgroups number their row blocks XCD by XCD, so the row
-//     blocks that read one vocabulary range share its W_lm lines in one L2.
-//   * Product. v_mfma_f32_16x16x32_bf16 with fp32 accumulation. Both operands are K-contiguous
-//     (rows of hidden for A, rows of W_lm for B): per step of 64 h a lane loads 16 consecutive
-//     h of each of its rows (32 bytes; a row's four lane groups read a whole 128-byte line) and
-//     feeds them to two MFMAs; four steps of loads are in flight (fewer for larger row tiles).
-//     H % 8 == 0; rows past R read row R - 1 and are dropped; tiles past a wave's run issue no
-//     loads.
-//   * Epilogue. The accumulator of tile (rt, ct) puts row 16 rt + 4 g + t (g = lane / 16) and
-//     column 16 ct + (lane % 16) in each lane, so every row lives in one lane group of 16. Each
-//     lane keeps an online logsumexp pair (reference = its largest value, log2 domain) per row;
-//     each row keeps its 16 best keys (the 64-bit candidate key) sorted across its lane group.
-//     A tile's keys are filtered against the larger of the list's 16th key and the smallest of
-//     the group's lane maxima (16 of the tile's keys reach it), and the survivors are inserted
-//     one per group per step (ballot rank, DPP row shift), all four groups at once.
-//   * End. The four waves' lists of each row are sorted together (64 keys) and the best 16 kept;
-//     their pairs are combined in wave order. Each workgroup writes [R][ranges] partials, and a
-//     second kernel merges a row's ranges (filtered insertion, pairs in range order). The whole
-//     path is deterministic.
+// Design (gfx950, wave64; one workgroup of eight waves per CU, R <= 16: the decode shape, where
+// W_lm is read once and the pass is bound by that read):
+//   * Work. A workgroup takes the (up to) 16 rows and a contiguous range of 16-column tiles of
+//     the vocabulary; a tile is 16 rows of W_lm, 16 H contiguous values. Wave w owns the 512-h
+//     chunks w, w + 8, ... of every tile of the range, so for H <= 4096 each wave holds the
+//     hidden rows' fragments of its chunk in registers for the whole pass (for a larger H a
+//     wave reloads them, from L2, for each of its chunks).
+//   * Stream. Per tile a wave reads, for each of the 16 rows, the row's 1 KB run of its chunk
+//     with one 16-byte nontemporal buffer load per lane (the eight waves together read each row
+//     whole); the next tile's loads are in flight while the current one is multiplied. Loads
+//     that cover 1 KB of one row each ran at 0.80 of the HBM peak on this access order; loads
+//     that cover 64 bytes of each of 16 rows (the layout an MFMA fragment wants) at 0.69.
+//   * Product. The wave writes its 16 runs to its own LDS area (rows padded by 16 bytes, so the
+//     reads below are free of bank conflicts) and reads them back as MFMA fragments: lane (n, kg)
+//     takes row n at h = 32 s + 8 kg of the chunk for k-slice s. v_mfma_f32_16x16x32_bf16 with
+//     fp32 accumulation over the chunk's 16 k-slices (K slot 8 kg + e is h = 32 s + 8 kg + e for
+//     both operands); h past H is zero on both sides.
+//   * Reduction. Each wave leaves its partial 16 x 16 tile in LDS (two buffers, one barrier per
+//     tile); wave i < 4 adds the waves' partials of rows 4 g + i (g < 4) in wave order and runs
+//     their epilogue, so four waves share it.
+//   * Epilogue (waves 0..3). The accumulator layout puts row 4 g + i (g = lane / 16, i < 4) and
+//     column lane % 16 in each lane, so every row lives in one lane group of 16. Each lane keeps an
+//     online logsumexp pair (reference = its largest value, log2 domain) per row; each row keeps
+//     its 16 best keys (the 64-bit candidate key) sorted across its lane group. Every four tiles
+//     the keys are filtered against the larger of the list's 16th key and the smallest of the
+//     group's lane maxima (16 of the offered keys reach it), and the survivors are inserted one
+//     per group per step (ballot rank, DPP row shift), or, when a group has more than four, sorted
+//     and merged.
+//   * End. Each workgroup writes [R][ranges] partials (a sorted list of 16 keys and a pair per
+//     row), and a second kernel merges a row's ranges. The whole path is deterministic.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -42,16 +48,19 @@ namespace dflash2 {
 namespace {
 
 
-constexpr int kLmWaves = 4;
+constexpr int kLmWaves = 8;            // waves per workgroup
 constexpr int kLmThreads = kLmWaves * kWave;
-constexpr int kLmGroup = 4;            // 16-column tiles per pass of a wave
+constexpr int kLmChunk = 512;          // h per chunk: a 1 KB run of each weight row
+constexpr int kLmSlices = kLmChunk / 32;  // k-slices (MFMAs) per chunk
+constexpr int kLmRowSlots = kLmChunk / 8 + 1;  // 16-byte slots per staged row, one of padding
+constexpr int kLmGroup = 4;            // tiles whose keys the epilogue offers at once
 constexpr int kLmList = 16;            // keys kept per row (>= k)
-constexpr int kLmRowTiles = 1;         // 16-row tiles per workgroup (R <= 16)
-constexpr int kLmTargetWgs = 512;      // workgroups per launch (about two per CU)
-constexpr int kXcds = 8;
+constexpr int kLmWgs = 256;            // workgroups per launch (the LDS holds one per CU)
+constexpr int kLmMaxRanges = 512;      // ranges per row the merge kernel takes at most
+constexpr int kBufWord3 = 0x00020000;  // gfx9-family buffer descriptor word 3 (raw data)
+constexpr int kNonTemp = 2;            // cache policy: streaming data, read once
 constexpr int kDppRowShr1 = 0x111;     // row_shr:1 (within rows of 16 lanes)
 constexpr int kDppRowLast = 0x15F;     // row_newbcast:15 (lane 15 of each row to the row)
-constexpr int kDppWaveShr1 = 0x138;    // wave_shr:1
 constexpr int kDppRowShl4 = 0x104;     // row_shl:4 (lane m reads m + 4)
 constexpr int kDppRowShr4 = 0x114;     // row_shr:4 (lane m reads m - 4)
 constexpr int kDppRowMirror = 0x140;   // row_mirror (lane m reads 15 - m)
@@ -69,13 +78,6 @@ __device__ __forceinline__ uint64_t dpp64(uint64_t v) {
 __device__ __forceinline__ uint64_t lane_read(uint64_t v, int src) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)(uint32_t)v);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)(uint32_t)(v >> 32));
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// Wave-uniform value of lane src (src uniform).
-__device__ __forceinline__ uint64_t lane_value(uint64_t v, int src) {
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, src);
-    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), src);
     return ((uint64_t)hi << 32) | lo;
 }
 
@@ -211,175 +213,146 @@ struct LmJob {
     const uint16_t *hidden;  // [R, H]
     const uint16_t *W;       // [V, H]
     int R, H, V;
-    int rblocks;             // row blocks of 16 * RT rows (one)
-    int ranges;              // vocabulary ranges (workgroups per row block)
+    int ranges;              // vocabulary ranges (one workgroup each)
     int col16;               // 16-column tiles in V
     uint64_t *part_keys;     // [R][ranges][kLmList]
     float2 *part_lse;        // [R][ranges] (log2-domain reference, sum)
 };
 
-// Workgroup (row block, range): the row block of one range on one XCD (see the header).
+// The hidden rows' MFMA fragments of chunk c: for k-slice s, lane (i, kg) holds h = 512 c + 32 s
+// + 8 kg .. + 7 of row i (zero past H and for rows past R).
+__device__ __forceinline__ void load_hidden_chunk(const LmJob &job, int c, int lane,
+                                                  u32x4 (&a)[kLmSlices]) {
+    const int i = lane & 15, kg = lane >> 4;
+    const bool row_ok = i < job.R;
+    const uint16_t *ar = job.hidden + (int64_t)(row_ok ? i : 0) * job.H;
+#pragma unroll
+    for (int s = 0; s < kLmSlices; ++s) {
+        const int h = kLmChunk * c + 32 * s + 8 * kg;
+        a[s] = row_ok && h < job.H ? *reinterpret_cast<const u32x4 *>(ar + h) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// Workgroup = one vocabulary range (see the header).
 __global__ __launch_bounds__(kLmThreads) void lmhead_topk_kernel(LmJob job) {
-    constexpr int RT = kLmRowTiles;
-    constexpr int D = 4;  // steps of loads in flight
-    __shared__ uint64_t lists[kLmWaves][16 * RT][16];
-    __shared__ float2 pairs[kLmWaves][16 * RT];
+    __shared__ u32x4 stage[kLmWaves][16][kLmRowSlots];  // each wave's chunk of the current tile
+    __shared__ f32x4 part[2][kLmWaves][kWave];          // the waves' partial tiles (two tiles)
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int m = lane & 15, g = lane >> 4;
-    const int n = (int)gridDim.x;
-    const int t = n % kXcds == 0 ? ((int)blockIdx.x % kXcds) * (n / kXcds) + (int)blockIdx.x / kXcds
-                                 : (int)blockIdx.x;
-    const int rb = t % job.rblocks, range = t / job.rblocks;
     const int H = job.H, V = job.V;
-    const int row0 = rb * 16 * RT;
-    const int nw = job.ranges * kLmWaves, gw = range * kLmWaves + wave;
-    const int tc0 = (int)((int64_t)job.col16 * gw / nw), tc1 = (int)((int64_t)job.col16 * (gw + 1) / nw);
+    const int range = blockIdx.x;
+    const int t0 = (int)((int64_t)job.col16 * range / job.ranges);
+    const int nt = (int)((int64_t)job.col16 * (range + 1) / job.ranges) - t0;
+    const int nc = (H + kLmChunk - 1) / kLmChunk;                          // chunks per tile
+    const int cpw = wave < nc ? (nc - 1 - wave) / kLmWaves + 1 : 0;        // this wave's
+    const int nwv = nc < kLmWaves ? nc : kLmWaves;                         // waves with a chunk
 
-    const uint16_t *arow[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-        arow[rt] = job.hidden + (int64_t)min(row0 + 16 * rt + m, job.R - 1) * H;
+    // (with one chunk per wave they stay for the whole pass; with more, each chunk reloads them)
+    u32x4 afr[kLmSlices];
+    if (cpw == 1) load_hidden_chunk(job, wave, lane, afr);
 
-    uint64_t list[RT][4];
-    float lref[RT][4], lsum[RT][4];
+    // Loads of chunk wave + 8 j of tile t0 + ti: stg[r] = row r's 16 bytes at h = 512 c + 8 lane
+    // (zero past H, and for rows past V: the descriptor ends at the last row).
+    u32x4 stg[16];
+    auto issue = [&](int ti, int j) {
+        const int tile = t0 + ti, c = wave + kLmWaves * j;
+        const int rows = min(16, V - tile * 16);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(job.W + (int64_t)tile * 16 * H), (short)0, rows * H * 2, kBufWord3);
+        const int h = kLmChunk * c + 8 * lane;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            list[rt][i] = 0ull;
-            lref[rt][i] = -INFINITY;
-            lsum[rt][i] = 0.f;
-        }
+        for (int r = 0; r < 16; ++r)
+            stg[r] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, h < H ? (r * H + h) * 2 : 0x7FFFFFF0,
+                                                             0, kNonTemp));
+    };
+    if (cpw > 0 && nt > 0) issue(0, 0);
 
-    const int ns = (H + 63) / 64;  // steps over H (two MFMAs each)
-    // passes of equal size (at most kLmGroup tiles): no pass much smaller than the others
-    const int npass = (tc1 - tc0 + kLmGroup - 1) / kLmGroup;
-    const int per = npass > 0 ? (tc1 - tc0 + npass - 1) / npass : kLmGroup;
-    for (int tc = tc0; tc < tc1; tc += per) {
-        const int te = min(tc + per, tc1);  // this pass: tiles tc .. te - 1
-        const uint16_t *brow[kLmGroup];
+    // Epilogue waves 0..3: wave i keeps row 4 g + i of the tile in lane group g.
+    const int ei = wave;  // (rows only for ei < 4)
+    uint64_t list = 0ull;
+    float lref = -INFINITY, lsum = 0.f, xs[kLmGroup];
 #pragma unroll
-        for (int c = 0; c < kLmGroup; ++c)
-            brow[c] = job.W + (int64_t)min((tc + c) * 16 + m, V - 1) * H;
-        f32x4 acc[RT][kLmGroup];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int c = 0; c < kLmGroup; ++c) acc[rt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < kLmGroup; ++c) xs[c] = 0.f;
 
-        // A step covers 64 of H: lane group g loads the 16 consecutive h at 64 s + 16 g of each
-        // row (32 bytes: four groups cover a 128-byte line), and the two MFMAs of the step take
-        // the first and the second 8 as their K slots 8 g .. 8 g + 7 (the same map for both
-        // operands, so the sum over h is unchanged). Tiles past the wave's run load nothing.
-        const int live = te - tc;
-        u32x4 fa[D][RT][2], fb[D][kLmGroup][2];
-        auto load = [&](int d, int s) {
-            const int kc = 64 * s + 16 * g;
-            const bool ok0 = kc < H, ok1 = kc + 8 < H;  // H % 8 == 0
+    for (int ti = 0; ti < nt; ++ti) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < cpw; ++j) {
+            // the chunk's rows to the wave's area, the next chunk's loads, then the MFMAs over
+            // the fragments read back (same wave: LDS operations complete in order)
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                fa[d][rt][0] = ok0 ? *reinterpret_cast<const u32x4 *>(arow[rt] + kc) : u32x4{0u, 0u, 0u, 0u};
-                fa[d][rt][1] = ok1 ? *reinterpret_cast<const u32x4 *>(arow[rt] + kc + 8) : u32x4{0u, 0u, 0u, 0u};
-            }
+            for (int r = 0; r < 16; ++r) stage[wave][r][lane] = stg[r];
+            if (j + 1 < cpw) issue(ti, j + 1);
+            else if (ti + 1 < nt) issue(ti + 1, 0);
+            if (cpw > 1) load_hidden_chunk(job, wave + kLmWaves * j, lane, afr);
 #pragma unroll
-            for (int c = 0; c < kLmGroup; ++c) {
-                const bool on = c < live;
-                fb[d][c][0] = on && ok0 ? *reinterpret_cast<const u32x4 *>(brow[c] + kc) : u32x4{0u, 0u, 0u, 0u};
-                fb[d][c][1] = on && ok1 ? *reinterpret_cast<const u32x4 *>(brow[c] + kc + 8) : u32x4{0u, 0u, 0u, 0u};
-            }
-        };
-#pragma unroll
-        for (int d = 0; d < D; ++d)
-            if (d < ns) load(d, d);
-        for (int s0 = 0; s0 < ns; s0 += D) {
-#pragma unroll
-            for (int d = 0; d < D; ++d) {
-                const int s = s0 + d;
-                if (s < ns) {
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                            for (int c = 0; c < kLmGroup; ++c)
-                                acc[rt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    __builtin_bit_cast(bf16x8, fa[d][rt][hf]),
-                                    __builtin_bit_cast(bf16x8, fb[d][c][hf]), acc[rt][c], 0, 0, 0);
-                    if (s + D < ns) load(d, s + D);
-                }
+            for (int s = 0; s < kLmSlices; ++s) {
+                const u32x4 b = stage[wave][m][4 * s + g];
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, afr[s]),
+                                                              __builtin_bit_cast(bf16x8, b), acc, 0,
+                                                              0, 0);
             }
         }
+        if (cpw > 0) part[ti & 1][wave][lane] = acc;
+        __syncthreads();
+        if (ei >= 4) continue;
 
-        // Epilogue: row 16 rt + 4 g + i, column (tc + c) * 16 + m.
+        // Epilogue: row 4 g + ei of the tile's logits (the waves' partials added in wave order),
+        // kept for a group of tiles.
+        const float *pp = reinterpret_cast<const float *>(&part[ti & 1][0][lane]) + ei;
+        float x = pp[0];
+        for (int w = 1; w < nwv; ++w) x += pp[w * kWave * 4];
+        const int slot = ti % kLmGroup;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
+        for (int c = 0; c < kLmGroup; ++c) xs[c] = slot == c ? x : xs[c];
+        if (slot != kLmGroup - 1 && ti != nt - 1) continue;
+        // column (tb + c) * 16 + m for the group's tiles c <= slot
+        const int tb = t0 + ti - slot;
+        uint64_t key[kLmGroup];
+        float xl[kLmGroup];
+        float xm = -INFINITY;
+        uint32_t vmax = 0u;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint64_t key[kLmGroup];
-                float xl[kLmGroup];
-                float xm = -INFINITY;
-                uint32_t vmax = 0u;
-#pragma unroll
-                for (int c = 0; c < kLmGroup; ++c) {
-                    const int col = (tc + c) * 16 + m;
-                    const bool ok = tc + c < te && col < V;
-                    const float x = acc[rt][c][i];
-                    key[c] = ok ? cand_key(x, col) : 0ull;
-                    xl[c] = ok ? x * kLog2e : -INFINITY;
-                    xm = fmaxf(xm, xl[c]);
-                    vmax = ok && (uint32_t)(key[c] >> 32) > vmax ? (uint32_t)(key[c] >> 32) : vmax;
-                }
-                if (xm != -INFINITY) {
-                    if (xm > lref[rt][i]) {
-                        lsum[rt][i] *= __builtin_amdgcn_exp2f(lref[rt][i] - xm);
-                        lref[rt][i] = xm;
-                    }
-                    float s = 0.f;
-#pragma unroll
-                    for (int c = 0; c < kLmGroup; ++c)
-                        s += xl[c] != -INFINITY ? __builtin_amdgcn_exp2f(xl[c] - lref[rt][i]) : 0.f;
-                    lsum[rt][i] += s;
-                }
-                const uint64_t tau0 = (uint64_t)row16_min(vmax) << 32;
-                offer_row(list[rt][i], key, tau0, lane);
-            }
+        for (int c = 0; c < kLmGroup; ++c) {
+            const int col = (tb + c) * 16 + m;
+            const bool ok = c <= slot && col < V;
+            key[c] = ok ? cand_key(xs[c], col) : 0ull;
+            xl[c] = ok ? xs[c] * kLog2e : -INFINITY;
+            xm = fmaxf(xm, xl[c]);
+            vmax = ok && (uint32_t)(key[c] >> 32) > vmax ? (uint32_t)(key[c] >> 32) : vmax;
         }
+        if (xm != -INFINITY) {
+            if (xm > lref) {
+                lsum *= __builtin_amdgcn_exp2f(lref - xm);
+                lref = xm;
+            }
+            float sacc = 0.f;
+#pragma unroll
+            for (int c = 0; c < kLmGroup; ++c)
+                sacc += xl[c] != -INFINITY ? __builtin_amdgcn_exp2f(xl[c] - lref) : 0.f;
+            lsum += sacc;
+        }
+        const uint64_t tau0 = (uint64_t)row16_min(vmax) << 32;
+        offer_row(list, key, tau0, lane);
     }
 
-    // The wave's lists and pairs to LDS; then each row's four lists are sorted together.
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rl = 16 * rt + 4 * g + i;
-            lists[wave][rl][m] = list[rt][i];
-            const float ref = row16_fmax(lref[rt][i]);
-            float s = ref == -INFINITY ? 0.f : lsum[rt][i] * __builtin_amdgcn_exp2f(lref[rt][i] - ref);
-            s = row16_sum(s);
-            if (m == 0) pairs[wave][rl] = make_float2(ref, s);
-        }
-    }
-    __syncthreads();
-    for (int rl = wave; rl < 16 * RT; rl += kLmWaves) {
-        const int row = row0 + rl;
-        if (row >= job.R) break;
-        uint64_t key = lists[lane >> 4][rl][lane & 15];
-        key = wave_sort_desc(key, lane);
-        const size_t part = (size_t)row * job.ranges + range;
-        if (lane < kLmList) job.part_keys[part * kLmList + lane] = key;
-        if (lane == 0) {
-            float ref = -INFINITY, sum = 0.f;
-#pragma unroll
-            for (int w = 0; w < kLmWaves; ++w) lse_combine(ref, sum, pairs[w][rl].x, pairs[w][rl].y);
-            job.part_lse[part] = make_float2(ref, sum);
-        }
+    // waves 0..3: each row's list (ranks in lane order) and pair to the range's partial
+    if (ei >= 4) return;
+    const int row = 4 * g + ei;
+    const float ref = row16_fmax(lref);
+    float sm = ref == -INFINITY ? 0.f : lsum * __builtin_amdgcn_exp2f(lref - ref);
+    sm = row16_sum(sm);
+    if (row < job.R) {
+        const size_t pi = (size_t)row * job.ranges + range;
+        job.part_keys[pi * kLmList + m] = list;
+        if (m == 0) job.part_lse[pi] = make_float2(ref, sm);
     }
 }
 
 // One workgroup of kMergeWaves waves per row; the row's ranges are each sorted lists of kLmList
-// keys. Wave w takes ranges [w, w + 1) * ranges / 16 (at most 32, as ranges <= kLmTargetWgs)
+// keys. Wave w takes ranges [w, w + 1) * ranges / 16 (at most 32, as ranges <= kLmMaxRanges)
 // and loads all their keys at once (lane j holds key j % 16 of ranges r0 + j / 16 + 4 s, s < 8:
 // one memory round trip). A threshold T: the k-th largest of the ranges' first (largest) keys,
 // which are distinct real keys, so the top k of the row are all >= T; and only the ranges whose
@@ -389,7 +362,7 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_topk_kernel(LmJob job) {
 // tree, then over the waves in order.
 constexpr int kMergeWaves = 16;
 constexpr int kMergeSteps = 8;  // 4 ranges per step: 32 ranges per wave
-static_assert(kMergeWaves * (kWave / kLmList) * kMergeSteps >= kLmTargetWgs,
+static_assert(kMergeWaves * (kWave / kLmList) * kMergeSteps >= kLmMaxRanges,
               "every range of a row has a load slot");
 constexpr int kMergeCands = kLmList * kWave;  // keys >= T at most
 
@@ -409,7 +382,7 @@ __device__ __forceinline__ uint64_t kth_largest(uint64_t v, int k) {
 // row's top k is >= T1) when at most 64 firsts reach it (the usual case), else the k-th largest
 // of all firsts (exactly k reach it).
 __device__ __forceinline__ uint64_t merge_threshold(const uint64_t *firsts, int k, int lane) {
-    constexpr int J = kLmTargetWgs / kWave;
+    constexpr int J = kLmMaxRanges / kWave;
     uint64_t f[J], m = 0ull;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -437,7 +410,7 @@ __device__ __forceinline__ uint64_t merge_threshold(const uint64_t *firsts, int 
 __global__ __launch_bounds__(kMergeWaves * kWave) void lmhead_merge_kernel(
     const uint64_t *__restrict__ part_keys, const float2 *__restrict__ part_lse, int ranges, int k,
     int32_t *__restrict__ cand_ids, float *__restrict__ unary, float *__restrict__ lse_out) {
-    __shared__ uint64_t firsts[kLmTargetWgs];   // each range's largest key (0: no range)
+    __shared__ uint64_t firsts[kLmMaxRanges];   // each range's largest key (0: no range)
     __shared__ uint64_t cands[kMergeCands];
     __shared__ uint32_t ncand;
     __shared__ uint64_t thr;
@@ -457,7 +430,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void lmhead_merge_kernel(
     const float2 pr = r0 + lane < r1 ? part_lse[(size_t)row * ranges + r0 + lane]
                                      : make_float2(-INFINITY, 0.f);
     if (threadIdx.x == 0) ncand = 0u;
-    for (int i = threadIdx.x; i < kLmTargetWgs; i += kMergeWaves * kWave) firsts[i] = 0ull;
+    for (int i = threadIdx.x; i < kLmMaxRanges; i += kMergeWaves * kWave) firsts[i] = 0ull;
     {  // (ref, sum) of the wave's ranges: lanes 0 .. r1 - r0 - 1, combined by a fixed tree
         float ref = pr.x, sum = pr.y;
 #pragma unroll
@@ -515,17 +488,14 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void lmhead_merge_kernel(
 }
 
 struct LmPlan {
-    int rblocks, ranges, col16;
+    int ranges, col16;
 };
 
 LmPlan plan_lmhead(int R, int V) {
+    (void)R;
     LmPlan p;
-    p.rblocks = (R + 16 * kLmRowTiles - 1) / (16 * kLmRowTiles);
     p.col16 = (V + 15) / 16;
-    int ranges = kLmTargetWgs / p.rblocks;
-    if (ranges < 1) ranges = 1;
-    const int most = (p.col16 + kLmWaves - 1) / kLmWaves;  // every wave gets a tile
-    p.ranges = ranges < most ? ranges : most;
+    p.ranges = p.col16 < kLmWgs ? p.col16 : kLmWgs;  // every workgroup gets a tile
     return p;
 }
 
@@ -548,14 +518,13 @@ hipError_t launch_lmhead_topk(const void *hidden, const void *W_lm, int R, int H
     job.R = R;
     job.H = H;
     job.V = V;
-    job.rblocks = p.rblocks;
     job.ranges = p.ranges;
     job.col16 = p.col16;
     job.part_keys = static_cast<uint64_t *>(workspace);
     job.part_lse = reinterpret_cast<float2 *>(job.part_keys + (size_t)R * p.ranges * kLmList);
-    if (R > 16 * kLmRowTiles) return hipErrorInvalidValue;  // the C ABI refuses these sizes
-    hipLaunchKernelGGL(lmhead_topk_kernel, dim3((unsigned)(job.rblocks * job.ranges)),
-                       dim3(kLmThreads), 0, stream, job);
+    if (R > 16) return hipErrorInvalidValue;  // the C ABI refuses these sizes
+    hipLaunchKernelGGL(lmhead_topk_kernel, dim3((unsigned)job.ranges), dim3(kLmThreads), 0, stream,
+                       job);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lmhead_merge_kernel, dim3((unsigned)R), dim3(kMergeWaves * kWave), 0, stream,

@@ -93,6 +93,8 @@ CASES = [
     (1, 8, 100, 1, 5),          # one row, one step, k = 1
     (16, 256, 3000, 8, 6),
     (9, 96, 4099, 16, 7),
+    (16, 4104, 2500, 16, 8),    # 9 chunks of 512 h: wave 0 takes two, the others one
+    (7, 8200, 1500, 8, 9),      # 17 chunks, the last of 8 h: two or three per wave
 ]
 
 
