@@ -30,7 +30,8 @@
 //     both operands); h past H is zero on both sides.
 //   * Reduction. Each wave leaves its partial 16 x 16 tile in LDS (two buffers, one barrier per
 //     tile); wave i < 4 adds the waves' partials of rows 4 g + i (g < 4) in wave order and runs
-//     their epilogue, so four waves share it.
+//     their epilogue, so four waves share it. A tile's epilogue runs during the next tile's
+//     iteration, after that iteration's loads are issued, so it overlaps their memory latency.
 //   * Epilogue (waves 0..3). The accumulator layout puts row 4 g + i (g = lane / 16, i < 4) and
 //     column lane % 16 in each lane, so every row lives in one lane group of 16. Each lane keeps an
 //     online logsumexp pair (reference = its largest value, log2 domain) per row; each row keeps
@@ -40,7 +41,8 @@
 //     per group per step (ballot rank, DPP row shift), or, when a group has more than four, sorted
 //     and merged.
 //   * End. Each workgroup writes [R][ranges] partials (a sorted list of 16 keys and a pair per
-//     row), and a second kernel merges a row's ranges. The whole path is deterministic.
+//     row), and a second kernel merges each row's ranges with one wave. The whole path is
+//     deterministic.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -56,7 +58,6 @@ constexpr int kLmRowSlots = kLmChunk / 8 + 1;  // 16-byte slots per staged row, 
 constexpr int kLmGroup = 4;            // tiles whose keys the epilogue offers at once
 constexpr int kLmList = 16;            // keys kept per row (>= k)
 constexpr int kLmWgs = 256;            // workgroups per launch (the LDS holds one per CU)
-constexpr int kLmMaxRanges = 512;      // ranges per row the merge kernel takes at most
 constexpr int kBufWord3 = 0x00020000;  // gfx9-family buffer descriptor word 3 (raw data)
 constexpr int kNonTemp = 2;            // cache policy: streaming data, read once
 constexpr int kDppRowShr1 = 0x111;     // row_shr:1 (within rows of 16 lanes)
@@ -215,8 +216,12 @@ struct LmJob {
     int R, H, V;
     int ranges;              // vocabulary ranges (one workgroup each)
     int col16;               // 16-column tiles in V
+    int k;
     uint64_t *part_keys;     // [R][ranges][kLmList]
     float2 *part_lse;        // [R][ranges] (log2-domain reference, sum)
+    int32_t *cand_ids;       // [R, k]
+    float *unary;            // [R, k]
+    float *lse_out;          // [R] or null
 };
 
 // The hidden rows' MFMA fragments of chunk c: for k-slice s, lane (i, kg) holds h = 512 c + 32 s
@@ -233,6 +238,109 @@ __device__ __forceinline__ void load_hidden_chunk(const LmJob &job, int c, int l
     }
 }
 
+// The k-th largest of the 64 lane values (one per lane, 0 = none, nonzero ones distinct): the
+// largest t with at least k lane values >= t, one bit at a time from the top.
+__device__ __forceinline__ uint64_t kth_largest(uint64_t v, int k) {
+    uint64_t t = 0ull;
+    for (int bit = 63; bit >= 0; --bit) {
+        const uint64_t c = t | (1ull << bit);
+        if (__popcll(__ballot(v >= c)) >= k) t = c;
+    }
+    return t;
+}
+
+constexpr int kLmRangesPerLane = kLmWgs / kWave;  // ranges a lane reads in the merge
+constexpr int kLmPoolKeys = kWave * kLmList;      // keys >= T at most (64 ranges' lists)
+
+// Row `row`'s merge by one wave: the ranges are each sorted lists of kLmList keys. T: the k-th
+// largest of the 64 lane-wise maxima of the ranges' first (largest) keys, which are distinct real
+// keys, so k of them reach T and every key of the row's first k is >= T; only ranges whose first
+// key reaches T hold such keys. When more than 64 firsts reach T, T becomes the exact k-th
+// largest first (then exactly k do). The chosen ranges' keys >= T go to LDS and are sorted 64 at
+// a time and merged. The ranges' pairs are combined per lane in range order, then by a fixed
+// lane tree. (pool: kLmPoolKeys keys, then 64 range indices.) Two dependent load rounds, no
+// barrier.
+__device__ __forceinline__ void merge_row(const LmJob &job, int row, uint64_t *pool, int lane) {
+    constexpr int Q = kLmRangesPerLane;
+    const int nr = job.ranges, k = job.k;
+    const uint64_t *pk = job.part_keys + (size_t)row * nr * kLmList;
+    const uint64_t *pl = reinterpret_cast<const uint64_t *>(job.part_lse + (size_t)row * nr);
+    uint64_t f[Q], pp[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int r = lane + kWave * q;
+        f[q] = r < nr ? pk[(size_t)r * kLmList] : 0ull;
+        pp[q] = r < nr ? pl[r] : 0ull;
+    }
+    float ref = -INFINITY, sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+        if (lane + kWave * q < nr)
+            lse_combine(ref, sum, __uint_as_float((uint32_t)pp[q]), __uint_as_float((uint32_t)(pp[q] >> 32)));
+#pragma unroll
+    for (int d = 1; d < kWave; d *= 2) {
+        const float oref = __shfl_down(ref, d, kWave), osum = __shfl_down(sum, d, kWave);
+        if (lane % (2 * d) == 0) lse_combine(ref, sum, oref, osum);
+    }
+    ref = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(ref)));
+    sum = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(sum)));
+
+    uint64_t mx = f[0];
+#pragma unroll
+    for (int q = 1; q < Q; ++q) mx = kmax(mx, f[q]);
+    uint64_t T = kth_largest(mx, k);
+    uint32_t n1 = 0u;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) n1 += (uint32_t)__popcll(__ballot(f[q] != 0ull && f[q] >= T));
+    if (n1 > (uint32_t)kWave) {  // many firsts at or above T: the exact k-th largest first
+        uint64_t t = 0ull;
+        for (int bit = 63; bit >= 0; --bit) {
+            const uint64_t c = t | (1ull << bit);
+            int n = 0;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) n += __popcll(__ballot(f[q] >= c));
+            if (n >= k) t = c;
+        }
+        T = t;
+    }
+    // the chosen ranges' indices (at most 64), then their keys >= T
+    uint32_t *idx = reinterpret_cast<uint32_t *>(pool + kLmPoolKeys);
+    uint32_t nsel = 0u;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const bool in = f[q] != 0ull && f[q] >= T;
+        const uint64_t m = __ballot(in);
+        if (in) idx[nsel + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] =
+            (uint32_t)(lane + kWave * q);
+        nsel += (uint32_t)__popcll(m);
+    }
+    const bool have = (uint32_t)lane < nsel;
+    const uint32_t rr = have ? idx[lane] : 0u;
+    uint64_t kk[kLmList];
+#pragma unroll
+    for (int i = 0; i < kLmList; ++i)
+        kk[i] = have ? pk[(size_t)rr * kLmList + i] : 0ull;
+    uint32_t n = 0u;
+#pragma unroll
+    for (int i = 0; i < kLmList; ++i) {
+        const bool in = kk[i] != 0ull && kk[i] >= T;
+        const uint64_t m = __ballot(in);
+        if (in) pool[n + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = kk[i];
+        n += (uint32_t)__popcll(m);
+    }
+    uint64_t top = 0ull;
+    for (uint32_t c0 = 0; c0 < n; c0 += kWave) {
+        const uint64_t c = c0 + lane < n ? pool[c0 + lane] : 0ull;
+        top = wave_merge_desc(top, wave_sort_desc(c, lane), lane);
+    }
+    const double lse = lse_value(ref, sum);
+    if (lane < k) {
+        job.cand_ids[row * k + lane] = key_id(top);
+        job.unary[row * k + lane] = (float)((double)key_logit(top) - lse);
+    }
+    if (lane == 0 && job.lse_out) job.lse_out[row] = (float)lse;
+}
+
 // Workgroup = one vocabulary range (see the header).
 __global__ __launch_bounds__(kLmThreads) void lmhead_topk_kernel(LmJob job) {
     __shared__ u32x4 stage[kLmWaves][16][kLmRowSlots];  // each wave's chunk of the current tile
@@ -243,6 +351,7 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_topk_kernel(LmJob job) {
     const int m = lane & 15, g = lane >> 4;
     const int H = job.H, V = job.V;
     const int range = blockIdx.x;
+    // the range's 16-column tiles [t0, t0 + nt)
     const int t0 = (int)((int64_t)job.col16 * range / job.ranges);
     const int nt = (int)((int64_t)job.col16 * (range + 1) / job.ranges) - t0;
     const int nc = (H + kLmChunk - 1) / kLmChunk;                          // chunks per tile
@@ -254,13 +363,15 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_topk_kernel(LmJob job) {
     if (cpw == 1) load_hidden_chunk(job, wave, lane, afr);
 
     // Loads of chunk wave + 8 j of tile t0 + ti: stg[r] = row r's 16 bytes at h = 512 c + 8 lane
-    // (zero past H, and for rows past V: the descriptor ends at the last row).
+    // (zero past H, and for rows past V: the descriptor ends at the last row, and reads past it
+    // return zero without a memory access; for ti = nt the descriptor is empty, so a load may be
+    // issued unconditionally, which keeps the compiler's waits for them exact).
     u32x4 stg[16];
     auto issue = [&](int ti, int j) {
-        const int tile = t0 + ti, c = wave + kLmWaves * j;
-        const int rows = min(16, V - tile * 16);
+        const int tv = 16 * (t0 + ti), c = wave + kLmWaves * j;
+        const int rows = ti < nt ? min(16, V - tv) : 0;  // past the range: an empty descriptor
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(job.W + (int64_t)tile * 16 * H), (short)0, rows * H * 2, kBufWord3);
+            const_cast<uint16_t *>(job.W + (int64_t)tv * H), (short)0, rows * H * 2, kBufWord3);
         const int h = kLmChunk * c + 8 * lane;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -277,39 +388,18 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_topk_kernel(LmJob job) {
 #pragma unroll
     for (int c = 0; c < kLmGroup; ++c) xs[c] = 0.f;
 
-    for (int ti = 0; ti < nt; ++ti) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < cpw; ++j) {
-            // the chunk's rows to the wave's area, the next chunk's loads, then the MFMAs over
-            // the fragments read back (same wave: LDS operations complete in order)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) stage[wave][r][lane] = stg[r];
-            if (j + 1 < cpw) issue(ti, j + 1);
-            else if (ti + 1 < nt) issue(ti + 1, 0);
-            if (cpw > 1) load_hidden_chunk(job, wave + kLmWaves * j, lane, afr);
-#pragma unroll
-            for (int s = 0; s < kLmSlices; ++s) {
-                const u32x4 b = stage[wave][m][4 * s + g];
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, afr[s]),
-                                                              __builtin_bit_cast(bf16x8, b), acc, 0,
-                                                              0, 0);
-            }
-        }
-        if (cpw > 0) part[ti & 1][wave][lane] = acc;
-        __syncthreads();
-        if (ei >= 4) continue;
-
-        // Epilogue: row 4 g + ei of the tile's logits (the waves' partials added in wave order),
-        // kept for a group of tiles.
-        const float *pp = reinterpret_cast<const float *>(&part[ti & 1][0][lane]) + ei;
+    // Epilogue of tile tt (waves 0..3): row 4 g + ei of its logits (the waves' partials added in
+    // wave order), kept for a group of tiles and offered when the group is full or the range ends.
+    auto epilogue = [&](int tt) {
+        const float *pp = reinterpret_cast<const float *>(&part[tt & 1][0][lane]) + ei;
         float x = pp[0];
         for (int w = 1; w < nwv; ++w) x += pp[w * kWave * 4];
-        const int slot = ti % kLmGroup;
+        const int slot = tt % kLmGroup;
 #pragma unroll
         for (int c = 0; c < kLmGroup; ++c) xs[c] = slot == c ? x : xs[c];
-        if (slot != kLmGroup - 1 && ti != nt - 1) continue;
+        if (slot != kLmGroup - 1 && tt != nt - 1) return;
         // column (tb + c) * 16 + m for the group's tiles c <= slot
-        const int tb = t0 + ti - slot;
+        const int tb = t0 + tt - slot;
         uint64_t key[kLmGroup];
         float xl[kLmGroup];
         float xm = -INFINITY;
@@ -336,7 +426,60 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_topk_kernel(LmJob job) {
         }
         const uint64_t tau0 = (uint64_t)row16_min(vmax) << 32;
         offer_row(list, key, tau0, lane);
+    };
+
+    // The chunk in stg to the wave's LDS area (the next loads may then reuse stg), and its 16
+    // MFMAs over the fragments read back (same wave: LDS operations complete in order).
+    auto stage_chunk = [&]() {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) stage[wave][r][lane] = stg[r];
+    };
+    auto mma_chunk = [&](f32x4 &acc) {
+#pragma unroll
+        for (int s = 0; s < kLmSlices; ++s) {
+            const u32x4 b = stage[wave][m][4 * s + g];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, afr[s]),
+                                                          __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+        }
+    };
+
+    // Tile ti: its chunks' products while the next tile's loads are in flight, then (waves 0..3)
+    // the previous tile's epilogue, still under those loads; the partial tile goes to buffer
+    // ti % 2, which the epilogue of tile ti - 2 (before the last barrier) has finished reading.
+    // Waves with one chunk (or none) and waves with several (H > 4096) run separate loops, so
+    // that in the first no load writes the fragments and the MFMAs never wait for the loads in
+    // flight.
+    if (cpw <= 1) {
+        for (int ti = 0; ti < nt; ++ti) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (cpw == 1) {
+                stage_chunk();
+                issue(ti + 1, 0);
+                __builtin_amdgcn_sched_barrier(0);  // the loads go out before the MFMAs
+                mma_chunk(acc);
+            }
+            if (ei < 4 && ti > 0) epilogue(ti - 1);
+            if (cpw == 1) part[ti & 1][wave][lane] = acc;
+            __syncthreads();
+        }
+    } else {
+        for (int ti = 0; ti < nt; ++ti) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < cpw; ++j) {
+                // (the next chunk's loads follow the MFMAs: the fragments and the loads in
+                // flight are not live together, which keeps this path within the registers)
+                stage_chunk();
+                load_hidden_chunk(job, wave + kLmWaves * j, lane, afr);
+                mma_chunk(acc);
+                const bool more = j + 1 < cpw;
+                issue(more ? ti : ti + 1, more ? j + 1 : 0);
+            }
+            if (ei < 4 && ti > 0) epilogue(ti - 1);
+            part[ti & 1][wave][lane] = acc;
+            __syncthreads();
+        }
     }
+    if (ei < 4 && nt > 0) epilogue(nt - 1);
 
     // waves 0..3: each row's list (ranks in lane order) and pair to the range's partial
     if (ei >= 4) return;
@@ -351,140 +494,10 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_topk_kernel(LmJob job) {
     }
 }
 
-// One workgroup of kMergeWaves waves per row; the row's ranges are each sorted lists of kLmList
-// keys. Wave w takes ranges [w, w + 1) * ranges / 16 (at most 32, as ranges <= kLmMaxRanges)
-// and loads all their keys at once (lane j holds key j % 16 of ranges r0 + j / 16 + 4 s, s < 8:
-// one memory round trip). A threshold T: the k-th largest of the ranges' first (largest) keys,
-// which are distinct real keys, so the top k of the row are all >= T; and only the ranges whose
-// first key is >= T hold keys >= T. Wave 0 finds T (below) such that at most 64 ranges reach it,
-// so at most kLmList * 64 keys pass; they go to LDS, and wave 0 sorts them (64 at a time,
-// merged) and keeps the top k. The (ref, sum) pairs are combined per wave by a fixed shuffle
-// tree, then over the waves in order.
-constexpr int kMergeWaves = 16;
-constexpr int kMergeSteps = 8;  // 4 ranges per step: 32 ranges per wave
-static_assert(kMergeWaves * (kWave / kLmList) * kMergeSteps >= kLmMaxRanges,
-              "every range of a row has a load slot");
-constexpr int kMergeCands = kLmList * kWave;  // keys >= T at most
-
-// The k-th largest of the 64 lane values (one per lane, 0 = none, nonzero ones distinct): the
-// largest t with at least k lane values >= t, one bit at a time from the top.
-__device__ __forceinline__ uint64_t kth_largest(uint64_t v, int k) {
-    uint64_t t = 0ull;
-    for (int bit = 63; bit >= 0; --bit) {
-        const uint64_t c = t | (1ull << bit);
-        if (__popcll(__ballot(v >= c)) >= k) t = c;
-    }
-    return t;
-}
-
-// A threshold for the n <= 512 distinct first keys in LDS (zeros elsewhere), by one wave: the
-// k-th largest T1 of the 64 lane-wise maxima (k distinct firsts reach it, so every key of the
-// row's top k is >= T1) when at most 64 firsts reach it (the usual case), else the k-th largest
-// of all firsts (exactly k reach it).
-__device__ __forceinline__ uint64_t merge_threshold(const uint64_t *firsts, int k, int lane) {
-    constexpr int J = kLmMaxRanges / kWave;
-    uint64_t f[J], m = 0ull;
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-        f[j] = firsts[lane + kWave * j];
-        m = kmax(m, f[j]);
-    }
-    const uint64_t t1 = kth_largest(m, k);
-    uint32_t n1 = 0u;
-#pragma unroll
-    for (int j = 0; j < J; ++j) n1 += (uint32_t)__popcll(__ballot(f[j] != 0ull && f[j] >= t1));
-    if (n1 > (uint32_t)kWave) {  // many firsts at or above T1: count all of them per bit
-        uint64_t t = 0ull;
-        for (int bit = 63; bit >= 0; --bit) {
-            const uint64_t c = t | (1ull << bit);
-            int n = 0;
-#pragma unroll
-            for (int j = 0; j < J; ++j) n += __popcll(__ballot(f[j] >= c));
-            if (n >= k) t = c;
-        }
-        return t;
-    }
-    return t1;
-}
-
-__global__ __launch_bounds__(kMergeWaves * kWave) void lmhead_merge_kernel(
-    const uint64_t *__restrict__ part_keys, const float2 *__restrict__ part_lse, int ranges, int k,
-    int32_t *__restrict__ cand_ids, float *__restrict__ unary, float *__restrict__ lse_out) {
-    __shared__ uint64_t firsts[kLmMaxRanges];   // each range's largest key (0: no range)
-    __shared__ uint64_t cands[kMergeCands];
-    __shared__ uint32_t ncand;
-    __shared__ uint64_t thr;
-    __shared__ float2 wp[kMergeWaves];
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t row = blockIdx.x;
-    const int r0 = ranges * wave / kMergeWaves, r1 = ranges * (wave + 1) / kMergeWaves;
-    constexpr int kPer = kWave / kLmList;  // ranges per step
-    uint64_t key[kMergeSteps];
-#pragma unroll
-    for (int st = 0; st < kMergeSteps; ++st) {
-        const int rr = r0 + lane / kLmList + kPer * st;
-        key[st] = rr < r1 ? part_keys[((size_t)row * ranges + rr) * kLmList + (lane % kLmList)]
-                          : 0ull;
-    }
-    const float2 pr = r0 + lane < r1 ? part_lse[(size_t)row * ranges + r0 + lane]
-                                     : make_float2(-INFINITY, 0.f);
-    if (threadIdx.x == 0) ncand = 0u;
-    for (int i = threadIdx.x; i < kLmMaxRanges; i += kMergeWaves * kWave) firsts[i] = 0ull;
-    {  // (ref, sum) of the wave's ranges: lanes 0 .. r1 - r0 - 1, combined by a fixed tree
-        float ref = pr.x, sum = pr.y;
-#pragma unroll
-        for (int d = 1; d < kWave / 2; d *= 2) {
-            const float oref = __shfl_down(ref, d, kWave), osum = __shfl_down(sum, d, kWave);
-            if (lane % (2 * d) == 0) lse_combine(ref, sum, oref, osum);
-        }
-        if (lane == 0) wp[wave] = make_float2(ref, sum);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int st = 0; st < kMergeSteps; ++st) {
-        const int rr = r0 + lane / kLmList + kPer * st;
-        if (lane % kLmList == 0 && rr < r1) firsts[rr] = key[st];
-    }
-    __syncthreads();
-    if (wave == 0) {
-        const uint64_t t = merge_threshold(firsts, k, lane);
-        if (lane == 0) thr = t;
-    }
-    __syncthreads();
-    const uint64_t T = thr;
-    // the keys >= T to LDS
-#pragma unroll
-    for (int st = 0; st < kMergeSteps; ++st) {
-        const bool pass = key[st] != 0ull && key[st] >= T;
-        const uint64_t m = __ballot(pass);
-        if (m == 0ull) continue;
-        uint32_t base = 0u;
-        if (lane == 0)
-            base = __hip_atomic_fetch_add(&ncand, (uint32_t)__popcll(m), __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_WORKGROUP);
-        base = __builtin_amdgcn_readfirstlane(base);
-        const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        if (pass) cands[base + rank] = key[st];
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    const uint32_t n = __builtin_amdgcn_readfirstlane(ncand);
-    uint64_t top = 0ull;
-    for (uint32_t c0 = 0; c0 < n; c0 += kWave) {
-        const uint64_t c = c0 + lane < n ? cands[c0 + lane] : 0ull;
-        top = wave_merge_desc(top, wave_sort_desc(c, lane), lane);
-    }
-    float ref = -INFINITY, sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kMergeWaves; ++w) lse_combine(ref, sum, wp[w].x, wp[w].y);
-    const double lse = lse_value(ref, sum);
-    if (lane < k) {
-        cand_ids[row * k + lane] = key_id(top);
-        unary[row * k + lane] = (float)((double)key_logit(top) - lse);
-    }
-    if (lane == 0 && lse_out) lse_out[row] = (float)lse;
+// One wave per row merges the row's ranges (merge_row).
+__global__ __launch_bounds__(kWave) void lmhead_merge_kernel(LmJob job) {
+    __shared__ uint64_t pool[kLmPoolKeys + kWave / 2];  // keys >= T, then 64 range indices
+    merge_row(job, (int)blockIdx.x, pool, (int)threadIdx.x);
 }
 
 struct LmPlan {
@@ -503,6 +516,7 @@ LmPlan plan_lmhead(int R, int V) {
 
 int lmhead_max_k() { return kLmList; }
 
+// [R][ranges] lists, then [R][ranges] pairs.
 size_t lmhead_workspace_bytes(int R, int V) {
     const LmPlan p = plan_lmhead(R, V);
     return (size_t)R * p.ranges * (kLmList * sizeof(uint64_t) + sizeof(float2));
@@ -520,15 +534,18 @@ hipError_t launch_lmhead_topk(const void *hidden, const void *W_lm, int R, int H
     job.V = V;
     job.ranges = p.ranges;
     job.col16 = p.col16;
+    job.k = k;
     job.part_keys = static_cast<uint64_t *>(workspace);
     job.part_lse = reinterpret_cast<float2 *>(job.part_keys + (size_t)R * p.ranges * kLmList);
+    job.cand_ids = cand_ids;
+    job.unary = unary;
+    job.lse_out = lse;
     if (R > 16) return hipErrorInvalidValue;  // the C ABI refuses these sizes
     hipLaunchKernelGGL(lmhead_topk_kernel, dim3((unsigned)job.ranges), dim3(kLmThreads), 0, stream,
                        job);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lmhead_merge_kernel, dim3((unsigned)R), dim3(kMergeWaves * kWave), 0, stream,
-                       job.part_keys, job.part_lse, p.ranges, k, cand_ids, unary, lse);
+    hipLaunchKernelGGL(lmhead_merge_kernel, dim3((unsigned)R), dim3(kWave), 0, stream, job);
     return hipGetLastError();
 }
 
