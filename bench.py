@@ -587,6 +587,9 @@ def main():
                     help="only loop K1 launches (for counter collection), no JSON")
     ap.add_argument("--select-only", action="store_true",
                     help="only loop selector calls (for counter collection), no JSON")
+    ap.add_argument("--lmhead-only", action="store_true",
+                    help="only loop LM-head top-k calls at lmhead-qwen3-8b-b1 (for profiling), "
+                         "no JSON")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="with --k1-only: also run device-to-device copies of this many MiB, the "
                          "calibration for the HBM byte counters")
@@ -614,6 +617,18 @@ def main():
         # (no time-based warm-up here: under a counter collection every launch is slow)
         ms = time_loop(w.step, args.steps, args.warmup, warm_seconds=0.0)
         log(f"[bench] select-only {args.workload}: {ms * 1e3:.2f} us/step")
+        return
+
+    if args.lmhead_only:
+        import dflash2_draft_candidate_amd as d2
+        ls = synth.LM_CONFIGS["lmhead-qwen3-8b-b1"]
+        hb, wb = synth.lmhead_inputs(ls.R, ls.H, ls.V, ls.seed)
+        h, wt = synth.as_torch(hb, device), synth.as_torch(wb, device)
+        del hb, wb
+        ms = time_loop(lambda i: d2.lmhead_topk(h, wt, ls.k), args.steps, args.warmup,
+                       warm_seconds=0.0)
+        log(f"[bench] lmhead-only {ls.name}: {ms * 1e3:.2f} us/call, "
+            f"{2 * ls.V * ls.H / (ms * 1e-3) / 1e9:.1f} GB/s of weight")
         return
 
     if args.k1_only:

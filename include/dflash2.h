@@ -258,9 +258,9 @@ int dflash2_dynconv(const void *x, const void *base, const void *dyn, int dtype,
  *   lse      [R]     fp32, device, out, may be NULL. logsumexp_v x[i][v].
  *   R >= 1; H >= 8 and H % 8 == 0; 1 <= V <= DFLASH2_MAX_V; 1 <= k <= min(V, DFLASH2_LMHEAD_MAX_K).
  *   R <= DFLASH2_LMHEAD_MAX_ROWS (decode: one 16-row tile, where the weight is read once and the
- *   pass is bound by that read); larger R returns DFLASH2_ERR_UNSUPPORTED: the pass stages no
- *   operand tiles in LDS, so once several row tiles reuse the weight a library product followed
- *   by dflash2_topk_lse is faster.
+ *   pass is bound by that read); larger R returns DFLASH2_ERR_UNSUPPORTED: the pass would read
+ *   the weight once per 16-row tile, and once several row tiles reuse it a library product
+ *   followed by dflash2_topk_lse is faster.
  * Workspace: dflash2_lmhead_topk_workspace_bytes(R, H, V, k) bytes (range partials), 16-byte
  * aligned, owned by the caller; contents need not be initialised (0 for sizes the pass refuses).
  * Errors: DFLASH2_ERR_INVALID_ARG, DFLASH2_ERR_UNSUPPORTED (R > DFLASH2_LMHEAD_MAX_ROWS),
