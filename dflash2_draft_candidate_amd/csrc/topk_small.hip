@@ -46,6 +46,8 @@ constexpr int kSmThreads = kSmWaves * kWave;
 constexpr int kSmVec = 4;            // 16-byte vectors per thread at most (one load round)
 constexpr int kSmMaxSlices = 64;     // slices per row at most (the merge reads S lists)
 constexpr int kSmTargetWgs = 256;    // workgroups resident at once (one per CU)
+constexpr int kSmSliceWgs = 128;     // slice workgroups the plan aims at: at 16 rows of 151936,
+                                     // 8 slices a row (12.0 us) beat 5, 6, 10, 12 and 16 (12.1-12.7)
 constexpr int kSmMinVecs = 64;       // a slice keeps at least this many vectors
 constexpr int kSmMaxNt = 8;          // gate tiles of up to 8 x 16 columns ride along
 constexpr int kSmCand = 4 * kWave;   // candidates a slice compacts for sorting, at most
@@ -479,7 +481,7 @@ bool plan_small(int R, int V, int elem_bytes, SmallPlanInfo &p) {
         p.slices = 1;
         return true;
     }
-    int64_t s = kSmTargetWgs / R;
+    int64_t s = kSmSliceWgs / R;
     const int64_t s_cap = nvec / kSmMinVecs;
     if (s > s_cap) s = s_cap;
     if (s > kSmMaxSlices) s = kSmMaxSlices;
