@@ -13,13 +13,15 @@ namespace {
 // Grid (B, passes): workgroup (b, c) covers positions of sequence b; with WALK it covers all of
 // them (c = 0) pass by pass, else pass c only. pp positions per pass, KT waves per position.
 // Dynamic LDS: the gate rows, [waves][rpad] floats.
-template <typename CB, int KT, bool WALK>
+// ONE (with WALK): the block is a single pass (L <= pp), known at compile time.
+template <typename CB, int KT, bool WALK, bool ONE>
 __global__ __launch_bounds__(lat_waves(KT, sizeof(CB)) * kWave) void lattice_kernel(LatArgs<CB> a) {
     extern __shared__ __attribute__((aligned(16))) float gsh[];
     __shared__ LatShared<WALK> ls;
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    lattice_sequence<CB, KT, WALK, false>(a, (int)blockIdx.x, (int)blockIdx.y, wave, lane, ls, gsh);
+    lattice_sequence<CB, KT, WALK, false, ONE>(a, (int)blockIdx.x, (int)blockIdx.y, wave, lane, ls,
+                                               gsh);
 }
 
 // Positions per pass for k and codebook element size cb: every wave of a workgroup busy.
@@ -32,7 +34,15 @@ int positions_per_pass(int L, int k, int cb) {
 
 template <typename CB, int KT, bool WALK>
 void launch_kt(dim3 grid, int waves, size_t lds, hipStream_t stream, const LatArgs<CB> &a) {
-    hipLaunchKernelGGL((lattice_kernel<CB, KT, WALK>), grid, dim3(waves * kWave), lds, stream, a);
+    if constexpr (WALK) {
+        if (a.L <= a.pp) {
+            hipLaunchKernelGGL((lattice_kernel<CB, KT, true, true>), grid, dim3(waves * kWave), lds,
+                               stream, a);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((lattice_kernel<CB, KT, WALK, false>), grid, dim3(waves * kWave), lds,
+                       stream, a);
 }
 
 template <typename CB, bool WALK>

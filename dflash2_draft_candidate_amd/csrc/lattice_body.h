@@ -191,10 +191,11 @@ struct LatArgs {
 };
 
 // The lattice of sequence b by the waves of one workgroup: with WALK every pass in turn and the
-// walk (every wave of the workgroup calls this: it holds barriers), else pass `pass_only`. pp
+// walk (every wave of the workgroup calls this: it holds barriers; ONE: a single pass), else pass
+// `pass_only`. pp
 // positions per pass, KT waves per position; waves past pp * KT take no position. gsh: the gate
 // rows, [pp * KT][rpad] floats.
-template <typename CB, int KT, bool WALK, bool COHERENT>
+template <typename CB, int KT, bool WALK, bool COHERENT, bool ONE = false>
 __device__ void lattice_sequence(const LatArgs<CB> &a, int b, int pass_only, int wave, int lane,
                                  LatShared<WALK> &ls, float *gsh) {
     const int32_t *__restrict__ cand_ids = a.cand_ids;
@@ -221,7 +222,12 @@ __device__ void lattice_sequence(const LatArgs<CB> &a, int b, int pass_only, int
     const int rpad = (r + kRankChunk - 1) / kRankChunk * kRankChunk;
     float *gw = gsh + (size_t)wave * rpad;
     const bool vec = (r % Seg<CB>::EV) == 0;
-    const int passes = WALK ? (L + pp - 1) / pp : 1;
+    // (ONE: the caller knows the block is one pass, L <= pp. Around a loop whose trip count is
+    // only known at run time the compiler hoists the body's invariant lane masks to the kernel's
+    // start and keeps them in spilled registers: several hundred instructions before each wave's
+    // first load, so that with four waves a SIMD the younger ones reached their loads
+    // microseconds late.)
+    const int passes = WALK && !ONE ? (L + pp - 1) / pp : 1;
     int prev = 0;  // walk: the chosen index at the previous position (the anchor's row is 0)
 
     for (int pass = 0; pass < passes; ++pass) {
