@@ -157,9 +157,10 @@ struct ThreadElems {
     }
 };
 
-// The candidate key of a compacted (logit bits, id) pair; 0 for an empty slot.
+// The candidate key of the compacted (logit bits, id) pair in a written slot (the pair of logit
+// +0 at id 0 is all zero bits, so zero cannot mark an empty slot).
 __device__ __forceinline__ uint64_t pair_key(uint64_t p) {
-    return p == 0ull ? 0ull : cand_key(__uint_as_float((uint32_t)(p >> 32)), (int32_t)(uint32_t)p);
+    return cand_key(__uint_as_float((uint32_t)(p >> 32)), (int32_t)(uint32_t)p);
 }
 
 // One gate tile (tile t = split sp * mtiles + m-tile mt): the first four waves compute it with the

@@ -61,6 +61,8 @@ def _logits(case, R, V, dtype, seed):
         x[zeros] = np.where(rng.random(zeros.sum()) < 0.5, -0.0, 0.0)
     elif case == "constant":
         x = np.full((R, V), 1.5)
+    elif case == "zeros":  # +0.0 everywhere: the (logit bits, id) pair of id 0 is all zero bits
+        x = np.zeros((R, V))
     elif case == "ascending":
         x = np.tile(np.linspace(-8, 8, V), (R, 1))
     elif case == "descending":
@@ -98,6 +100,9 @@ TOPK_CASES = [
     ("signed_zero", 6, 2000, 24, "f32"),
     ("signed_zero", 6, 2000, 24, "bf16"),
     ("constant", 3, 4096, 8, "f32"),
+    ("zeros", 3, 100, 8, "f32"),
+    ("zeros", 2, 3000, 16, "bf16"),
+    ("zeros", 300, 2000, 4, "f32"),
     ("ascending", 2, 20000, 16, "f32"),
     # every element beats the threshold so far: 8 (then 2) units share a workgroup's queue, which
     # fills up (slots reserved in bulk, waves keeping their own lists, the owner's sorted drains)
