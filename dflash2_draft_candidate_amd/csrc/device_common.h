@@ -89,20 +89,22 @@ constexpr int kDppRowRor8 = 0x128;
 constexpr int kDppRowRor12 = 0x12C;
 constexpr int kDppRowMirror = 0x140;  // lane l reads lane 15 - l of its row
 
+// (Every lane's source exists for these patterns, so the moves take no old value: with one,
+// the compiler first clears the destination, an extra instruction per move.)
 template <int S>
 __device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane) {
     static_assert(S == 1 || S == 2 || S == 4 || S == 8 || S == 16 || S == 32, "lane xor");
     if constexpr (S == 1)
-        return __builtin_amdgcn_update_dpp(0u, v, kDppQuadXor1, 0xF, 0xF, false);
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppQuadXor1, 0xF, 0xF, true);
     if constexpr (S == 2)
-        return __builtin_amdgcn_update_dpp(0u, v, kDppQuadXor2, 0xF, 0xF, false);
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppQuadXor2, 0xF, 0xF, true);
     if constexpr (S == 4) {
-        const uint32_t up = __builtin_amdgcn_update_dpp(0u, v, kDppRowRor12, 0xF, 0xF, false);
-        const uint32_t dn = __builtin_amdgcn_update_dpp(0u, v, kDppRowRor4, 0xF, 0xF, false);
+        const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppRowRor12, 0xF, 0xF, true);
+        const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppRowRor4, 0xF, 0xF, true);
         return (lane & 4) ? dn : up;
     }
     if constexpr (S == 8)
-        return __builtin_amdgcn_update_dpp(0u, v, kDppRowRor8, 0xF, 0xF, false);
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppRowRor8, 0xF, 0xF, true);
     if constexpr (S == 16) {
         const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
         return (lane & 16) ? r[0] : r[1];
@@ -122,9 +124,9 @@ __device__ __forceinline__ uint64_t xor_lane64(uint64_t v, int lane) {
 
 // Lane l receives lane 63 - l: the row mirror (l ^ 15 within a row), then l ^ 16 and l ^ 32.
 __device__ __forceinline__ uint64_t reverse_lanes64(uint64_t v, int lane) {
-    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, kDppRowMirror, 0xF, 0xF, false);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, kDppRowMirror, 0xF, 0xF, true);
     const uint32_t hi =
-        __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), kDppRowMirror, 0xF, 0xF, false);
+        (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), kDppRowMirror, 0xF, 0xF, true);
     return xor_lane64<32>(xor_lane64<16>(((uint64_t)hi << 32) | lo, lane), lane);
 }
 
@@ -134,12 +136,13 @@ __device__ __forceinline__ uint64_t kmax(uint64_t a, uint64_t b) { return a > b 
 __device__ __forceinline__ uint64_t kmin(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
 // One compare-exchange step with the partner l ^ S: the lower lane of the pair keeps the
-// larger key when `desc`, the smaller otherwise.
+// larger key when `desc`, the smaller otherwise (one compare decides which of the two it keeps;
+// equal keys are the same either way).
 template <int S>
 __device__ __forceinline__ uint64_t bitonic_step(uint64_t key, int lane, bool desc) {
     const uint64_t other = xor_lane64<S>(key, lane);
-    const bool lower = (lane & S) == 0;
-    return (lower == desc) ? kmax(key, other) : kmin(key, other);
+    const bool keep_max = ((lane & S) == 0) == desc;
+    return ((key > other) == keep_max) ? key : other;
 }
 
 // Compare-exchange steps with the partners l ^ S, l ^ S/2, ..., l ^ 1 (one bitonic merge).
@@ -178,10 +181,10 @@ constexpr int kDppRor8 = 0x128;  // row_ror:8
 // Sum over each row of 16 lanes, in every lane of the row (rotations: each lane adds the same
 // values in a different order; every partial is a sum of distinct lanes).
 __device__ __forceinline__ float row16_sum(float v) {
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRor8, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRor4, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppXor2, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppXor1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kDppRor8, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kDppRor4, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kDppXor2, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kDppXor1, 0xF, 0xF, true));
     return v;
 }
 

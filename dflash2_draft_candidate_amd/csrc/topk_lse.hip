@@ -98,11 +98,13 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-// Lane i receives lane i - 1's value (lane 0 receives 0).
+// Lane i receives lane i - 1's value (lane 0 receives 0: it has no source, and the bound
+// control writes zero there, with no cleared destination needed).
 __device__ __forceinline__ uint64_t shift_up_one(uint64_t v) {
-    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, kDppWaveShr1, 0xF, 0xF, false);
-    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), kDppWaveShr1, 0xF,
-                                                    0xF, false);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, kDppWaveShr1, 0xF, 0xF,
+                                                           true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), kDppWaveShr1,
+                                                           0xF, 0xF, true);
     return ((uint64_t)hi << 32) | lo;
 }
 

@@ -89,7 +89,8 @@ __device__ __forceinline__ uint64_t pick64(uint64_t v, int src) {
 template <int S>
 __device__ __forceinline__ uint32_t u32_merge_steps(uint32_t v, int lane, bool desc) {
     const uint32_t o = xor_lane<S>(v, lane);
-    v = (((lane & S) == 0) == desc) ? max(v, o) : min(v, o);
+    const bool keep_max = ((lane & S) == 0) == desc;
+    v = ((v > o) == keep_max) ? v : o;
     if constexpr (S > 1) v = u32_merge_steps<S / 2>(v, lane, desc);
     return v;
 }
