@@ -406,7 +406,12 @@ __device__ void lattice_sequence(const LatArgs<CB> &a, int b, int pass_only, int
                 const int src = lane < k ? lane : 0;
                 const u32x4 bw = *reinterpret_cast<const u32x4 *>(&best_s[buf][src][0]);
                 const uint32_t bj[kLatWaves / 4] = {bw.x, bw.y, bw.z, bw.w};
-                int out_j = 0;
+                // Every step runs (no branch per step): past np the bytes are stale and only
+                // steer v_readlane (which reads lane index & 63) until the loop ends; prev keeps
+                // the step np - 1 choice for the next pass. The choice of step q (< 64) goes to
+                // byte q of four wave-uniform words, which lane q reads at the end.
+                uint32_t pj[kLatWaves / 4] = {0u, 0u, 0u, 0u};
+                int cur = prev;
                 if (p_min > 0.f) {
                     float cf[kLatWaves];
 #pragma unroll
@@ -417,27 +422,27 @@ __device__ void lattice_sequence(const LatArgs<CB> &a, int b, int pass_only, int
                     }
 #pragma unroll
                     for (int q = 0; q < kLatWaves; ++q) {
-                        if (q < np) {
-                            const float c = __uint_as_float(
-                                __builtin_amdgcn_readlane(__float_as_uint(cf[q]), prev));
-                            if (stop == L && c < p_min) stop = p0 + q;
-                            const int j = (int)((__builtin_amdgcn_readlane(bj[q / 4], prev) >>
-                                                 (8 * (q % 4))) & 0xFFu);
-                            out_j = lane == q ? j : out_j;
-                            prev = j;
-                        }
+                        const float c = __uint_as_float(
+                            __builtin_amdgcn_readlane(__float_as_uint(cf[q]), cur));
+                        stop = (q < np && stop == L && c < p_min) ? p0 + q : stop;
+                        const int j = (int)((__builtin_amdgcn_readlane(bj[q / 4], cur) >>
+                                             (8 * (q % 4))) & 0xFFu);
+                        pj[q / 4] |= (uint32_t)j << (8 * (q % 4));
+                        prev = q == np - 1 ? j : prev;
+                        cur = j;
                     }
                 } else {
 #pragma unroll
                     for (int q = 0; q < kLatWaves; ++q) {
-                        if (q < np) {
-                            const int j = (int)((__builtin_amdgcn_readlane(bj[q / 4], prev) >>
-                                                 (8 * (q % 4))) & 0xFFu);
-                            out_j = lane == q ? j : out_j;
-                            prev = j;
-                        }
+                        const int j = (int)((__builtin_amdgcn_readlane(bj[q / 4], cur) >>
+                                             (8 * (q % 4))) & 0xFFu);
+                        pj[q / 4] |= (uint32_t)j << (8 * (q % 4));
+                        prev = q == np - 1 ? j : prev;
+                        cur = j;
                     }
                 }
+                const uint32_t pw = lane < 4 ? pj[0] : lane < 8 ? pj[1] : lane < 12 ? pj[2] : pj[3];
+                const int out_j = (int)((pw >> (8 * (lane & 3))) & 0xFFu);
                 if (lane < np) {
                     path[(int64_t)b * L + p0 + lane] = cand_s[buf][lane][out_j];
                     if (path_idx) path_idx[(int64_t)b * L + p0 + lane] = out_j;
