@@ -27,6 +27,10 @@ namespace {
 constexpr int kTargetWgs = 256;
 constexpr int kMaxSplits = 8;  // the consumer adds at most this many partials, all loads at once
 
+// Steps in flight per wave in the stand-alone kernel (a step holds 4 + 8 * max(1, NT / 2)
+// registers): 8 (one round trip at H = 4096 with 4 splits) up to 8 column tiles, 4 at 16.
+template <int NT> constexpr int kAloneSteps = NT <= 8 ? 8 : 4;
+
 template <int NT>
 __global__ __launch_bounds__(gate_waves<NT>() * kWave) void gate_bf16_kernel(
     const uint16_t *__restrict__ hidden, const uint16_t *__restrict__ W, int R, int H, int r,
@@ -40,7 +44,8 @@ __global__ __launch_bounds__(gate_waves<NT>() * kWave) void gate_bf16_kernel(
     int s0, s1;
     gate_steps(H, blockIdx.y * GW + wave, splits * GW, s0, s1);
     f32x4 acc[NT];
-    gate_wave<NT>(hidden, W, R, H, r, blockIdx.x * 16, s0, s1, lane, acc);
+    // (alone, the kernel's registers allow more steps in flight than inside the top-k pass)
+    gate_wave<NT, kAloneSteps<NT>, true>(hidden, W, R, H, r, blockIdx.x * 16, s0, s1, lane, acc);
 
     // acc[t][i]: row g*4+i of the tile, column out_col(t, m). Sum the GW waves in order.
 #pragma unroll

@@ -124,12 +124,15 @@ __device__ __forceinline__ void gate_steps(int H, int q, int nq, int &s0, int &s
 // One wave's part of a tile: rows row0 .. row0 + 15 (rows past R read row R - 1 and are dropped
 // at the store) over steps [s0, s1). acc[t][i] is row g*4+i, column out_col(t, m) of the tile,
 // with m = lane & 15 and g = lane >> 4.
-template <int NT>
+// DB: steps whose loads are issued together; TAIL: a last batch of fewer steps stays on the
+// fast path (else it goes step by step). The MFMAs run in step order either way, so every
+// choice gives the same sums bit for bit.
+template <int NT, int DB = batch_steps<NT>(), bool TAIL = false>
 __device__ __forceinline__ void gate_wave(const uint16_t *__restrict__ hidden,
                                           const uint16_t *__restrict__ W, int R, int H, int r,
                                           int row0, int s0, int s1, int lane, f32x4 *acc) {
     constexpr int NC = NT * 16;
-    constexpr int D = batch_steps<NT>();
+    constexpr int D = DB;
     const int m = lane & 15, g = lane >> 4;
     const int row = row0 + m;
     const bool row_ok = row < R;
@@ -147,6 +150,20 @@ __device__ __forceinline__ void gate_wave(const uint16_t *__restrict__ hidden,
                 load_step<NT, true>(st[d], hrow, row_ok, W, H, r, (s + d) * kStepK, g, m);
 #pragma unroll
             for (int d = 0; d < D; ++d) mma_step<NT>(st[d], acc);
+        }
+        if constexpr (TAIL) {
+            // the remaining n < D steps that lie inside H, in one batch (uniform conditions)
+            const int n = min(s1, H / kStepK) - s;
+            if (n > 0) {
+                Step<NT> st[D];
+#pragma unroll
+                for (int d = 0; d < D; ++d)
+                    if (d < n) load_step<NT, true>(st[d], hrow, row_ok, W, H, r, (s + d) * kStepK, g, m);
+#pragma unroll
+                for (int d = 0; d < D; ++d)
+                    if (d < n) mma_step<NT>(st[d], acc);
+                s += n;
+            }
         }
     }
     for (; s < s1; ++s) {
