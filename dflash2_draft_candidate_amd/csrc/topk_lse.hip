@@ -174,7 +174,10 @@ __device__ __forceinline__ void gate_tile_part(const GateJob &gj, int gw, int la
     constexpr int GW = gate_waves<NT>();
     gate_steps(gj.H, sp * GW + gw, gj.splits * GW, s0, s1);
     f32x4 acc[NT];
-    gate_wave<NT>(gj.hidden, gj.W, gj.R, gj.H, gj.r, mt * 16, s0, s1, lane, acc);
+    // (four steps of loads in flight up to 4 column tiles: the stream's registers are not live
+    // yet; at 8 tiles two would spill)
+    gate_wave<NT, NT <= 4 ? 4 : batch_steps<NT>(), NT <= 4>(gj.hidden, gj.W, gj.R, gj.H, gj.r,
+                                                              mt * 16, s0, s1, lane, acc);
     const int m = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
