@@ -234,7 +234,8 @@ __device__ __forceinline__ void load_hidden_chunk(const LmJob &job, int c, int l
 #pragma unroll
     for (int s = 0; s < kLmSlices; ++s) {
         const int h = kLmChunk * c + 32 * s + 8 * kg;
-        a[s] = row_ok && h < job.H ? *reinterpret_cast<const u32x4 *>(ar + h) : u32x4{0u, 0u, 0u, 0u};
+        a[s] = row_ok && h < job.H ? *reinterpret_cast<const u32x4 *>(ar + h)
+                                   : u32x4{0u, 0u, 0u, 0u};
     }
 }
 
@@ -276,7 +277,8 @@ __device__ __forceinline__ void merge_row(const LmJob &job, int row, uint64_t *p
 #pragma unroll
     for (int q = 0; q < Q; ++q)
         if (lane + kWave * q < nr)
-            lse_combine(ref, sum, __uint_as_float((uint32_t)pp[q]), __uint_as_float((uint32_t)(pp[q] >> 32)));
+            lse_combine(ref, sum, __uint_as_float((uint32_t)pp[q]),
+                        __uint_as_float((uint32_t)(pp[q] >> 32)));
 #pragma unroll
     for (int d = 1; d < kWave; d *= 2) {
         const float oref = __shfl_down(ref, d, kWave), osum = __shfl_down(sum, d, kWave);
@@ -310,8 +312,10 @@ __device__ __forceinline__ void merge_row(const LmJob &job, int row, uint64_t *p
     for (int q = 0; q < Q; ++q) {
         const bool in = f[q] != 0ull && f[q] >= T;
         const uint64_t m = __ballot(in);
-        if (in) idx[nsel + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] =
-            (uint32_t)(lane + kWave * q);
+        if (in)
+            idx[nsel + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] =
+                (uint32_t)(lane + kWave * q);
         nsel += (uint32_t)__popcll(m);
     }
     const bool have = (uint32_t)lane < nsel;
@@ -325,7 +329,9 @@ __device__ __forceinline__ void merge_row(const LmJob &job, int row, uint64_t *p
     for (int i = 0; i < kLmList; ++i) {
         const bool in = kk[i] != 0ull && kk[i] >= T;
         const uint64_t m = __ballot(in);
-        if (in) pool[n + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = kk[i];
+        if (in)
+            pool[n + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = kk[i];
         n += (uint32_t)__popcll(m);
     }
     uint64_t top = 0ull;
