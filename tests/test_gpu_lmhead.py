@@ -95,6 +95,8 @@ CASES = [
     (9, 96, 4099, 16, 7),
     (16, 4104, 2500, 16, 8),    # 9 chunks of 512 h: wave 0 takes two, the others one
     (7, 8200, 1500, 8, 9),      # 17 chunks, the last of 8 h: two or three per wave
+    (3, 64, 5, 5, 10),          # fewer vocabulary rows than one tile (k = V)
+    (16, 520, 17, 16, 11),      # two tiles, the second of one row; H a 512-h chunk plus 8
 ]
 
 
