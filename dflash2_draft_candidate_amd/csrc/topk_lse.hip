@@ -17,12 +17,12 @@
 //   * Streaming. Lanes read 16-byte vectors (consecutive lanes, consecutive vectors) through a
 //     buffer descriptor bounded to the unit (an offset past it reads zeros), with a ring of
 //     kRing batches in registers, kRing - 1 issued ahead of the one processed.
-//   * logsumexp with a fixed reference. The unit's reference R (log2 domain) is the largest lane
-//     maximum seen by the seed below. Each lane sums 2^(x log2e - R) over a chunk (one v_exp per
-//     element, no per-batch rescale) and stores the sum to LDS; the sums are added per lane in
-//     chunk order at the end, so the result does not depend on which wave took which chunk. A
-//     chunk whose sum leaves the safe fp32 range (an element far above every seeded maximum)
-//     sends the unit down a slow exact path at the end.
+//   * logsumexp with a fixed reference. Each lane sums 2^(x log2e) (a reference of 0 in the log2
+//     domain: one v_exp per element, no per-batch rescale) over a chunk and stores the sum to
+//     LDS; the sums are added per lane in chunk order at the end, so the result does not depend
+//     on which wave took which chunk. A chunk whose sum leaves the safe fp32 range (logits above
+//     about 69) or a row total too small to keep its precision sends the unit down a slow exact
+//     path at the end.
 //   * top-k. A 64-bit key (order-preserving logit map above the inverted id) makes the candidate
 //     order one unsigned compare. The unit's oldest wave (its owner) keeps the unit's 64 best
 //     keys sorted across its lanes; the other waves queue their candidates to it through LDS,
