@@ -98,12 +98,21 @@ def _dtype(t: torch.Tensor) -> int:
     raise TypeError(f"expected float32 or bfloat16, got {t.dtype}")
 
 
+# Every entry point declares its pointer arguments as c_void_p, so plain integers (and None for
+# NULL) are passed as they are: no ctypes object is built per argument.
 def _ptr(t: torch.Tensor | None):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
-def _stream(device: torch.device):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(device: torch.device) -> int:
+    """The current stream of `device` as a raw handle."""
+    index = device.index if device.index is not None else torch.cuda.current_device()
+    if _raw_stream is not None:
+        return _raw_stream(index)
+    return torch.cuda.current_stream(index).cuda_stream
 
 
 def _check(rc: int, what: str):
@@ -115,7 +124,7 @@ def _contig(*ts: torch.Tensor):
     for t in ts:
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
-        if t.device.type != "cuda":
+        if not t.is_cuda:
             raise ValueError("tensors must live on the GPU")
 
 
@@ -150,9 +159,8 @@ def select(logits: torch.Tensor, hidden: torch.Tensor, W_sel: torch.Tensor,
                torch.empty((B, L, k, k), dtype=torch.float32, device=dev),
                torch.empty((B, L), dtype=torch.int32, device=dev))
     cand_ids, unary, edges, path = out
-    need = workspace_bytes(B, L, V, H, r, k)
     if workspace is None:
-        workspace = _workspace(need, dev)
+        workspace = _workspace(workspace_bytes(B, L, V, H, r, k), dev)
     rc = _lib.dflash2_select(_ptr(logits), _dtype(logits), _ptr(hidden), _dtype(hidden),
                              _ptr(W_sel), _ptr(pred_cb), _ptr(succ_cb), _dtype(pred_cb),
                              _ptr(anchor_ids), B, L, V, H, r, k, _ptr(cand_ids), _ptr(unary),
