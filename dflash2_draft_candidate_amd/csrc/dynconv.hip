@@ -63,10 +63,12 @@ dynconv_vec_kernel(
     constexpr int kRows = rows_ahead(KT);
     const int ncb = (C / EV + kConvThreads - 1) / kConvThreads;  // column groups
     const int nseg = (Tn + kRows - 1) / kRows;
-    const int64_t seg_all = blockIdx.x / ncb;
-    const int v = (int)(blockIdx.x % ncb) * kConvThreads + threadIdx.x;  // vector of channels
-    const int64_t b = seg_all / nseg;
-    const int t0 = (int)(seg_all % nseg) * kRows;
+    // (32-bit index arithmetic: a 64-bit division is hundreds of scalar instructions before the
+    // first load; the grid's block count fits 32 bits)
+    const uint32_t seg_all = blockIdx.x / (uint32_t)ncb;
+    const int v = (int)(blockIdx.x % (uint32_t)ncb) * kConvThreads + threadIdx.x;  // channel vector
+    const int64_t b = seg_all / (uint32_t)nseg;
+    const int t0 = (int)(seg_all % (uint32_t)nseg) * kRows;
     const int c0 = v * EV;
     if (c0 >= C) return;
     const int ng = C / G;

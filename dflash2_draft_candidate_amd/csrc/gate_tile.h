@@ -114,11 +114,13 @@ __device__ __forceinline__ void mma_step(const Step<NT> &s, f32x4 *acc) {
 template <int NT> constexpr int batch_steps() { return NT <= 2 ? 4 : (NT == 4 ? 2 : 1); }
 
 
-// Steps [s0, s1) of wave q of the nq waves that share a tile's H (q = split * 4 + wave).
+// Steps [s0, s1) of wave q of the nq waves that share a tile's H (q = split * 4 + wave). In
+// 32 bits: nsteps < 2^26 and q < nq <= 64, so the products fit (a 64-bit division costs hundreds
+// of scalar instructions before the wave's first load).
 __device__ __forceinline__ void gate_steps(int H, int q, int nq, int &s0, int &s1) {
-    const int nsteps = (H + kStepK - 1) / kStepK;
-    s0 = (int)((int64_t)nsteps * q / nq);
-    s1 = (int)((int64_t)nsteps * (q + 1) / nq);
+    const uint32_t nsteps = (uint32_t)(H + kStepK - 1) / kStepK;
+    s0 = (int)(nsteps * (uint32_t)q / (uint32_t)nq);
+    s1 = (int)(nsteps * (uint32_t)(q + 1) / (uint32_t)nq);
 }
 
 // One wave's part of a tile: rows row0 .. row0 + 15 (rows past R read row R - 1 and are dropped
