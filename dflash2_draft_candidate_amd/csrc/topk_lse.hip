@@ -7,13 +7,14 @@
 // section "What llama.cpp Actually Builds for the Selector" (per-position top-k, gathered unary).
 //
 // Design (gfx950, wave64). A unit is a (row, slice) pair (S slices per row; S = 1 unless rows
-// are too few to fill the chip, and then a second kernel merges the slices in slice order). One
-// workgroup of 16 waves fills a CU and owns G units; W = 16 / G waves stream each unit.
+// are too few to fill the chip, and then a second kernel merges the slices in slice order). Two
+// workgroups of 8 waves share a CU (each owns G <= 4 units; W = 8 / G waves stream each unit):
+// a workgroup whose units are done leaves its SIMDs to the other one, which one 16-wave
+// workgroup per CU could not do (its waves waited for its slowest unit).
 //   * Balance. The SIMD issues oldest-first, so with a static split the youngest wave on each
-//     SIMD finished far behind the oldest. Here a unit's waves are taken from different age
-//     classes (slots w, w + 4, ... sit on one SIMD with ages 0, 1, ...), so every unit streams at
-//     the same total rate, and they share the unit's chunks (CB batches of 4 vectors per lane)
-//     through an LDS counter, so a favoured wave simply takes more chunks.
+//     SIMD finished far behind the oldest. Here a unit's waves share the unit's chunks (CB
+//     batches of 4 vectors per lane) through an LDS counter, so a favoured wave simply takes
+//     more chunks, and a wave whose unit has none left helps another unit of its workgroup.
 //   * Streaming. Lanes read 16-byte vectors (consecutive lanes, consecutive vectors) through a
 //     buffer descriptor bounded to the unit (an offset past it reads zeros), with a ring of
 //     kRing batches in registers, kRing - 1 issued ahead of the one processed.
@@ -52,7 +53,7 @@
 //     four to finish sums their parts through LDS and stores the tile. The work sharing lets the
 //     other twelve waves absorb the delay. A gate rides along only where its tile parts fit in
 //     LDS beside the chunk sums of the pass's own plan (so select and the stage-by-stage calls
-//     sum the same chunks). Tiles are numbered XCD by XCD (see xcd_major).
+//     sum the same chunks). Tiles are numbered XCD by XCD (see gate_tile_of).
 #include <atomic>
 
 #include "device_common.h"
@@ -66,13 +67,14 @@ namespace {
 constexpr int kU = 4;                     // 16-byte vectors per lane per batch
 constexpr int kStep = kU * kWave;         // vectors per batch
 constexpr int kRing = 3;                  // batch buffers per wave (kRing - 1 loads ahead)
-constexpr int kWaves = 16;                // waves per workgroup: one workgroup fills a CU
+constexpr int kWaves = 8;                 // waves per workgroup: two workgroups fill a CU
 constexpr int kThreads = kWaves * kWave;
-constexpr int kMaxUnits = 8;              // units per workgroup (W = kWaves / G >= 2)
-constexpr int kTargetWorkgroups = 256;    // one per CU
+constexpr int kMaxUnits = 4;              // units per workgroup (W = kWaves / G >= 2)
+constexpr int kTargetWorkgroups = 512;    // two per CU
+constexpr int kSliceBelowRows = 256;      // fewer rows than this are cut into slices
 constexpr int kMinBatchesPerWave = 1;     // slices are not cut smaller than this per wave
-constexpr size_t kLdsBudget = 120 * 1024; // chunk sums per workgroup (dynamic LDS)
-constexpr size_t kLdsDynamicMax = 136 * 1024;  // chunk sums + a fused gate's tile parts
+constexpr size_t kLdsBudget = 56 * 1024;  // chunk sums per workgroup (dynamic LDS)
+constexpr size_t kLdsDynamicMax = 66 * 1024;  // chunk sums + a fused gate's tile parts
 constexpr float kSumLimit = 0x1p100f;     // a chunk sum above this leaves the fast path
 constexpr float kSumFloor = 0x1p-60f;     // so does a unit total below this
 constexpr float kTermMargin = 1.f - 0x1p-10f;  // v_exp_f32 is far more accurate than this
@@ -130,7 +132,8 @@ struct K1Shared {
     uint32_t unit_nch[kMaxUnits];     // and its chunks (0: no unit)
     uint32_t done_all;                // waves that have finished the stream
 };
-static_assert(sizeof(K1Shared) + kLdsDynamicMax <= 160 * 1024, "LDS of a CU (gfx950)");
+static_assert(sizeof(K1Shared) + kLdsDynamicMax <= 80 * 1024,
+              "two workgroups share the 160 KB of LDS of a CU (gfx950)");
 
 static_assert(kLdsDynamicMax >= kLdsBudget, "the chunk sums always fit");
 
@@ -143,10 +146,9 @@ struct GateJob {
     int R, H, r, mtiles, splits;
 };
 
-// The gate waves: four slots of one age class, one per SIMD, none of them a unit's owner (age 1;
-// age 2 when a unit has two waves). The oldest class would keep the owners busy, and the youngest
-// gets too few issue slots to finish its tile early.
-template <int G> constexpr int gate_first_wave() { return G == 8 ? 8 : 4; }
+// The gate waves: slots 4-7, one per SIMD, none of them a unit's owner (owners are the slots
+// below G <= 4).
+template <int G> constexpr int gate_first_wave() { return 4; }
 
 template <int NT>
 constexpr size_t gate_red_floats() {
@@ -158,8 +160,13 @@ constexpr size_t gate_red_floats() {
 // W_sel slices), so each XCD's L2 fetches the W_sel slices it needs once instead of every
 // XCD fetching all of W_sel for every m-tile.
 constexpr int kXcds = 8;
-__device__ __forceinline__ int xcd_major(int g, int n) {
-    return n % kXcds == 0 ? (g % kXcds) * (n / kXcds) + g / kXcds : g;
+// The gate tile of workgroup g of n (-1: none) when there are T <= n tiles: the first
+// T / kXcds workgroups of each XCD take that XCD's run of consecutive tiles, so the tiles spread
+// evenly over the XCDs (and, dispatched first, over the CUs).
+__device__ __forceinline__ int gate_tile_of(int g, int n, int T) {
+    if (T % kXcds != 0 || n % kXcds != 0) return g < T ? g : -1;
+    const int j = g / kXcds;
+    return j < T / kXcds ? (g % kXcds) * (T / kXcds) + j : -1;
 }
 
 // Wave gw (0..3) of the workgroup's gate tile; the last of the four stores the tile.
@@ -167,8 +174,8 @@ template <int NT>
 __device__ __forceinline__ void gate_tile_part(const GateJob &gj, int gw, int lane, float *red,
                                             uint32_t *arrived) {
     constexpr int PITCH = gate_pitch<NT>();
-    const int t = xcd_major(blockIdx.x, gridDim.x);
-    if (t >= gj.mtiles * gj.splits) return;
+    const int t = gate_tile_of(blockIdx.x, gridDim.x, gj.mtiles * gj.splits);
+    if (t < 0) return;
     const int mt = t % gj.mtiles, sp = t / gj.mtiles;
     int s0, s1;
     constexpr int GW = gate_waves<NT>();
@@ -506,17 +513,11 @@ __device__ __forceinline__ void batch(const u32x4 *buf, int nvalid, int32_t id_b
 // on SIMD s % 4 with age s / 4) so that every unit gets the same mix; and the inverse.
 template <int G>
 __device__ __forceinline__ void wave_unit(int s, int &q, int &wv) {
-    if (G == 8) {  // pairs of ages (0, 3) and (1, 2)
-        q = s < 8 ? s : 15 - s;
-        wv = s < 8 ? 0 : 1;
-    } else {
-        q = s % G;
-        wv = s / G;
-    }
+    q = s % G;
+    wv = s / G;
 }
 template <int G>
 __device__ __forceinline__ int unit_slot(int q, int wv) {
-    if (G == 8) return wv == 0 ? q : 15 - q;
     return q + G * wv;
 }
 
@@ -739,7 +740,8 @@ topk_lse_kernel(const T *__restrict__ logits, int V, int k, int S, int n_units, 
     // waves nearly cover waits for the unit threshold before it offers anything (a short wait
     // that spares the owner most of the candidates); a longer unit does not wait, nor does one
     // with at most one batch per wave (the threshold would come after every batch is read).
-    const bool has_tile = NTG > 0 && xcd_major(blockIdx.x, gridDim.x) < gj.mtiles * gj.splits;
+    const bool has_tile =
+        NTG > 0 && gate_tile_of(blockIdx.x, gridDim.x, gj.mtiles * gj.splits) >= 0;
     auto gate_slot = [&](int s) {
         return has_tile && s >= gate_first_wave<G>() && s < gate_first_wave<G>() + gate_waves<NTG>();
     };
@@ -1033,8 +1035,7 @@ hipError_t launch_k1(const TopkPlan &plan, const void *logits, int R, int V, int
     switch (plan.groups) {
     case 1: launch_g<T, 1>(plan, nt, grid, lds, stream, x, V, k, units, cand_ids, unary, lse, part_keys, part_lse, gj); break;
     case 2: launch_g<T, 2>(plan, nt, grid, lds, stream, x, V, k, units, cand_ids, unary, lse, part_keys, part_lse, gj); break;
-    case 4: launch_g<T, 4>(plan, nt, grid, lds, stream, x, V, k, units, cand_ids, unary, lse, part_keys, part_lse, gj); break;
-    default: launch_g<T, 8>(plan, nt, grid, lds, stream, x, V, k, units, cand_ids, unary, lse, part_keys, part_lse, gj); break;
+    default: launch_g<T, 4>(plan, nt, grid, lds, stream, x, V, k, units, cand_ids, unary, lse, part_keys, part_lse, gj); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.slices == 1) return e;
@@ -1050,10 +1051,10 @@ TopkPlan plan_topk(int R, int V, int elem_bytes) {
     const int64_t nvec_row = V / EV + 1;  // whole vectors of a row, rounded up
     const int64_t nb_row = (nvec_row + kStep - 1) / kStep;
     TopkPlan p;
-    // Slices only when rows are fewer than workgroups, and never below kMinBatchesPerWave
-    // batches per wave.
+    // Slices only for fewer than kSliceBelowRows rows (enough slices for a unit per
+    // workgroup), and never below kMinBatchesPerWave batches per wave.
     int64_t s = 1;
-    if (R < kTargetWorkgroups) {
+    if (R < kSliceBelowRows) {
         s = (kTargetWorkgroups + R - 1) / R;
         const int64_t s_max = nb_row / ((int64_t)kWaves * kMinBatchesPerWave);
         if (s > s_max) s = s_max;
