@@ -104,7 +104,7 @@ TOPK_CASES = [
     ("zeros", 2, 3000, 16, "bf16"),
     ("zeros", 300, 2000, 4, "f32"),
     ("ascending", 2, 20000, 16, "f32"),
-    # every element beats the threshold so far: 8 (then 2) units share a workgroup's queue, which
+    # every element beats the threshold so far: 4 units (then 1) share a workgroup's queue, which
     # fills up (slots reserved in bulk, waves keeping their own lists, the owner's sorted drains)
     ("ascending", 2048, 6000, 64, "bf16"),
     ("ascending", 600, 20000, 32, "f32"),
